@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of CLEAR attention forward on one MI355X.
+
+One step = one CLEAR attention layer (image-query tiles, text rows, and the
+text-row merge) over Q, K, V already resident in HBM.  The workload is the
+8192x8192 FLUX-1.dev shape: B 1, 24 heads, head_dim 128, a 512x512 token grid
+plus 512 text tokens, bf16, seeded synthetic inputs (the generator of
+dit_circular_local_amd.inputs).  The headline radius is r = 32; r = 8 is timed
+the same way and reported alongside.
+
+Metric: in-window attention TFLOP/s = 4 * d * (admitted pairs) * B * H / time,
+counting only pairs the mask admits (image-window pairs, image->text pairs, and
+the global text rows), as a fraction of the bf16 dense matrix-core peak.
+
+Prints ONE JSON line on stdout (progress goes to stderr).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 matrix-core peak (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def admitted_pairs(n_text: int, gh: int, gw: int, r2: int) -> int:
+    """Admitted (query, key) pairs of one head: for each window offset (dy, dx)
+    with dy^2 + dx^2 <= r2, (gh - |dy|)(gw - |dx|) image queries have that key on
+    the grid; image queries also admit the n_text text keys; text queries admit
+    all N keys."""
+    img = 0
+    if r2 >= 0:
+        w = math.isqrt(r2)
+        for dy in range(-w, w + 1):
+            if abs(dy) >= gh:
+                continue
+            half = math.isqrt(r2 - dy * dy)
+            for dx in range(-half, half + 1):
+                if abs(dx) < gw:
+                    img += (gh - abs(dy)) * (gw - abs(dx))
+    n = n_text + gh * gw
+    return img + gh * gw * n_text + n_text * n
+
+
+def computed_pairs(ca, n_text: int, gh: int, gw: int, r2: int) -> int:
+    """Pairs the kernels actually evaluate (tile waste included), from the tile map."""
+    import numpy as np
+
+    tm = ca.tile_map_build(gh, gw, r2)
+    f = tm["flags"].astype(np.int64)
+    per_wave_img = sum(int(((f >> w) & 1).sum()) for w in range(4)) * ca.CHUNK * 32
+    ntx = -(-gw // ca.TILE_W)
+    nty = -(-gh // ca.TILE_H)
+    waves_on = sum(min(4, max(0, -(-(gh - ty * 16) // 4))) for ty in range(nty)) * ntx
+    text_keys = -(-n_text // ca.CHUNK) * ca.CHUNK
+    n = n_text + gh * gw
+    text_rows = -(-n_text // 128) * 128 * (-(-n // ca.CHUNK) * ca.CHUNK)
+    return per_wave_img + waves_on * 32 * text_keys + text_rows
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dit_circular_local_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, radius: int):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    e = t.get(f"{workload}_r{radius}")
+    if not e or e.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def time_layer(ca, torch, q, k, v, w, radius, steps, warmup):
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ca.fwd(q, k, v, w.n_text, w.grid_h, w.grid_w, radius=radius, out=out)   # builds the tile map
+    torch.cuda.synchronize()
+    first_ms = (time.perf_counter() - t0) * 1e3
+    for _ in range(warmup):
+        ca.fwd(q, k, v, w.n_text, w.grid_h, w.grid_w, radius=radius, out=out)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        ca.fwd(q, k, v, w.n_text, w.grid_h, w.grid_w, radius=radius, out=out)
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ker = sorted(s.elapsed_time(e) for s, e in ev)
+    return {
+        "ms_per_step": wall_ms,
+        "kernel_ms_mean": sum(ker) / len(ker),
+        "kernel_ms_p10": ker[int(0.1 * (len(ker) - 1))],
+        "kernel_ms_median": ker[len(ker) // 2],
+        "kernel_ms_p90": ker[int(0.9 * (len(ker) - 1))],
+        "first_call_ms": first_ms,
+    }, out
+
+
+def cpu_baseline(q, k, v, w, radius, budget_s):
+    """The fp64 oracle, untuned, on a bounded sample of the same layer: head 0,
+    its first 64 text rows, then 8x8 image blocks spread over the grid until the
+    time budget is spent.  Reported in the metric's unit (in-window TFLOP/s)."""
+    import numpy as np
+    from oracle import attention_head, in_window_pairs
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    qh = q[0, 0].float().cpu().numpy()
+    kh = k[0, 0].float().cpu().numpy()
+    vh = v[0, 0].float().cpu().numpy()
+    r2 = radius * radius
+    nby, nbx = -(-w.grid_h // 8), -(-w.grid_w // 8)
+    order = np.random.default_rng(0).permutation(nby * nbx)
+    text_rows = list(range(min(64, w.n_text)))
+    t0 = time.perf_counter()
+    attention_head(qh, kh, vh, w.n_text, w.grid_h, w.grid_w, r2, text_rows=text_rows, blocks=[])
+    done = []
+    i = 0
+    while time.perf_counter() - t0 < budget_s and i < len(order):
+        batch = [(int(b) // nbx, int(b) % nbx) for b in order[i:i + 16]]
+        attention_head(qh, kh, vh, w.n_text, w.grid_h, w.grid_w, r2, text_rows=[], blocks=batch)
+        done += batch
+        i += 16
+    secs = time.perf_counter() - t0
+    pairs = in_window_pairs(w.n_text, w.grid_h, w.grid_w, r2, text_rows=text_rows, blocks=done)
+    tflops = 4.0 * w.d * pairs / secs / 1e12
+    return {
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"head 0 of 24: {len(text_rows)} text rows + {len(done)} of {nby * nbx} 8x8 image "
+                  f"blocks (r={radius}), {pairs} admitted pairs in {secs:.1f} s, fp64 numpy",
+        "seconds": secs,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="flux8k")
+    ap.add_argument("--radius", type=int, default=32)
+    ap.add_argument("--also-radius", type=int, default=8, help="second radius timed alongside (-1: none)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) is not supported: "
+              "the CLEAR attention layer here runs on a single MI355X", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dit_circular_local_amd as ca
+    from dit_circular_local_amd.inputs import WORKLOADS, workload_qkv
+
+    w = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    log(f"generating {w.name} inputs (seeded)...")
+    t0 = time.perf_counter()
+    q, k, v = workload_qkv(w, seed=0, device="cuda")
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    results = {}
+    radii = [args.radius] + ([args.also_radius] if args.also_radius >= 0 and args.also_radius != args.radius else [])
+    for r in radii:
+        t, _ = time_layer(ca, torch, q, k, v, w, r, args.steps, args.warmup)
+        pairs = admitted_pairs(w.n_text, w.grid_h, w.grid_w, r * r)
+        flops = 4.0 * w.d * pairs * w.B * w.H
+        cpairs = computed_pairs(ca, w.n_text, w.grid_h, w.grid_w, r * r)
+        t["in_window_tflops"] = flops / (t["ms_per_step"] * 1e-3) / 1e12
+        t["pct_bf16_peak"] = 100.0 * t["in_window_tflops"] / PEAK_BF16_TFLOPS
+        t["computed_tflops"] = 4.0 * w.d * cpairs * w.B * w.H / (t["ms_per_step"] * 1e-3) / 1e12
+        t["flops_per_layer"] = flops
+        t["admitted_pairs_per_head"] = pairs
+        t["computed_pairs_per_head"] = cpairs
+        results[r] = t
+        log(f"r={r}: {t['ms_per_step']:.3f} ms/layer, {t['in_window_tflops']:.1f} TFLOP/s in-window "
+            f"({t['pct_bf16_peak']:.1f}% of bf16 peak), kernel {t['kernel_ms_mean']:.3f} ms")
+
+    main_r = args.radius
+    m = results[main_r]
+    achieved = m["flops_per_layer"] / (m["kernel_ms_mean"] * 1e-3) / 1e12
+    traffic = load_traffic(w.name, main_r)
+    line = {
+        "metric": "in-window attention TFLOP/s (CLEAR forward, 8192x8192, r=32; ms/layer and r=8 alongside)",
+        "value": round(m["in_window_tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(m["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"CLEAR attention forward {w.name}: B{w.B} H{w.H} d{w.d}, "
+                        f"{w.grid_h}x{w.grid_w} grid + {w.n_text} text tokens, r={main_r}",
+            "B": w.B, "H": w.H, "d": w.d, "n_text": w.n_text, "grid_h": w.grid_h, "grid_w": w.grid_w,
+            "radius": main_r,
+        },
+        "pct_bf16_peak": round(m["pct_bf16_peak"], 2),
+        "ms_per_layer": {"median": round(m["kernel_ms_median"], 4), "p10": round(m["kernel_ms_p10"], 4),
+                         "p90": round(m["kernel_ms_p90"], 4)},
+        "computed_tflops": round(m["computed_tflops"], 3),
+        "tilemap_first_call_ms": round(m["first_call_ms"], 3),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "clear_attn_fwd_kernel<Bf16<128>> + clear_text_merge_kernel (HIP events around each call)",
+        },
+    }
+    for r in radii[1:]:
+        t = results[r]
+        line[f"r{r}"] = {
+            "ms_per_layer": round(t["ms_per_step"], 4),
+            "in_window_tflops": round(t["in_window_tflops"], 3),
+            "pct_bf16_peak": round(t["pct_bf16_peak"], 2),
+            "computed_tflops": round(t["computed_tflops"], 3),
+        }
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle on a sample (~{args.cpu_seconds:.0f} s)...")
+        line["cpu_baseline"] = cpu_baseline(q, k, v, w, main_r, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,213 @@
-"""CLEAR circular-window attention for AMD Instinct MI355X (gfx950)."""
+"""CLEAR circular-window attention for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding of ``libclear_attn.so`` (C ABI in ``include/clear_attn.h``).
+This module only marshals arguments: every step of the attention runs in the
+library's HIP kernels.  PyTorch supplies device memory and the stream.  If the
+library has not been built, every call raises (there is no fallback).
+
+    from dit_circular_local_amd import fwd
+    out = fwd(q, k, v, n_text=512, grid_h=64, grid_w=64, radius=16)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "ClearError", "fwd", "tile_map_size", "tile_map_build", "tile_map_build_device",
+    "release_cache", "last_error", "version", "lib", "EXPORTS",
+    "CLEAR_OK", "CLEAR_EINVAL", "CLEAR_ENOMEM", "CLEAR_EHIP", "CLEAR_ENOTSUP",
+    "CLEAR_BF16", "CLEAR_FP32", "TILE_H", "TILE_W", "SUB_H", "SUB_W", "CHUNK", "MAX_GRID",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libclear_attn.so")
+
+CLEAR_OK, CLEAR_EINVAL, CLEAR_ENOMEM, CLEAR_EHIP, CLEAR_ENOTSUP = 0, -22, -12, -5, -95
+CLEAR_BF16, CLEAR_FP32 = 0, 1
+TILE_H, TILE_W, SUB_H, SUB_W, CHUNK = 16, 8, 4, 8, 32
+MAX_GRID = 8192
+
+# every entry point declared in include/clear_attn.h
+EXPORTS = (
+    "clear_attn_fwd", "clear_attn_fwd_ex", "clear_tile_map_size", "clear_tile_map_build",
+    "clear_tile_map_build_device", "clear_last_error", "clear_release_cache", "clear_version",
+)
+
+
+class ClearError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class _Opts(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("r2_max", ctypes.c_int),
+                ("lse_out", ctypes.c_void_p), ("text_splits", ctypes.c_int)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "(or python dit_circular_local_amd/build.py)")
+    L = ctypes.CDLL(LIB_PATH)
+    i, p, sz, szp = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)
+    L.clear_attn_fwd.argtypes = [p, p, p, p, i, i, i, i, i, i, i, p]
+    L.clear_attn_fwd.restype = i
+    L.clear_attn_fwd_ex.argtypes = [p, p, p, p, i, i, i, i, i, i, ctypes.POINTER(_Opts), p]
+    L.clear_attn_fwd_ex.restype = i
+    L.clear_tile_map_size.argtypes = [i, i, i, i, i, i, i, i, szp, szp]
+    L.clear_tile_map_size.restype = i
+    L.clear_tile_map_build.argtypes = [i, i, i, i, i, i, i, i, p, p, sz, p, p, sz, szp, szp]
+    L.clear_tile_map_build.restype = i
+    L.clear_tile_map_build_device.argtypes = [i, i, i, i, i, i, i, i, p, p, sz, p, p, sz, szp, szp, p]
+    L.clear_tile_map_build_device.restype = i
+    L.clear_last_error.argtypes = []
+    L.clear_last_error.restype = ctypes.c_char_p
+    L.clear_release_cache.argtypes = []
+    L.clear_release_cache.restype = None
+    L.clear_version.argtypes = []
+    L.clear_version.restype = i
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return lib().clear_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != CLEAR_OK:
+        raise ClearError(rc, last_error())
+
+
+def version() -> int:
+    return lib().clear_version()
+
+
+def release_cache() -> None:
+    lib().clear_release_cache()
+
+
+def _stream_of(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def fwd(q, k, v, n_text: int, grid_h: int, grid_w: int, radius: Optional[int] = None,
+        r2: Optional[int] = None, out=None, return_lse: bool = False, text_splits: int = 0,
+        use_ex: Optional[bool] = None):
+    """CLEAR attention forward on torch tensors [B, H, N, d] (bf16 or fp32, on the GPU).
+
+    Give either ``radius`` (r2 = radius^2, the "<=" reading) or ``r2`` directly
+    (e.g. radius^2 - 1 for the strict "<" reading, -1 for no image keys).
+    Returns ``out`` or ``(out, lse)``.
+    """
+    import torch
+
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    if q.dtype == torch.bfloat16:
+        dtype = CLEAR_BF16
+    elif q.dtype == torch.float32:
+        dtype = CLEAR_FP32
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all be [B, H, N, d]")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be GPU tensors")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    if N != n_text + grid_h * grid_w:
+        raise ValueError(f"N = {N} != n_text + grid_h * grid_w = {n_text + grid_h * grid_w}")
+    if (radius is None) == (r2 is None):
+        raise ValueError("give exactly one of radius and r2")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    stream = _stream_of(q)
+    L = lib()
+    if use_ex is None:
+        use_ex = not (dtype == CLEAR_BF16 and r2 is None and not return_lse and text_splits == 0)
+    if not use_ex:
+        rc = L.clear_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              B, H, d, n_text, grid_h, grid_w, int(radius), stream)
+    else:
+        if r2 is None:
+            if radius < 0:
+                raise ValueError("radius must be >= 0")
+            r2 = min(int(radius) * int(radius), 2 ** 31 - 1)
+        opts = _Opts(dtype, int(r2), lse.data_ptr() if lse is not None else None, int(text_splits))
+        rc = L.clear_attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 B, H, d, n_text, grid_h, grid_w, ctypes.byref(opts), stream)
+    _check(rc)
+    return (out, lse) if return_lse else out
+
+
+def tile_map_size(grid_h, grid_w, r2, tile_h=TILE_H, tile_w=TILE_W, sub_h=SUB_H, sub_w=SUB_W,
+                  chunk=CHUNK):
+    nr, nc = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().clear_tile_map_size(grid_h, grid_w, r2, tile_h, tile_w, sub_h, sub_w, chunk,
+                                     ctypes.byref(nr), ctypes.byref(nc)))
+    return nr.value, nc.value
+
+
+def _ntiles(grid_h, grid_w, tile_h, tile_w):
+    return (-(-grid_h // tile_h)) * (-(-grid_w // tile_w))
+
+
+def tile_map_build(grid_h, grid_w, r2, tile_h=TILE_H, tile_w=TILE_W, sub_h=SUB_H, sub_w=SUB_W,
+                   chunk=CHUNK):
+    """Host-built tile map as numpy arrays (layout in include/clear_attn.h)."""
+    L = lib()
+    nr, nc = tile_map_size(grid_h, grid_w, r2, tile_h, tile_w, sub_h, sub_w, chunk)
+    nt = _ntiles(grid_h, grid_w, tile_h, tile_w)
+    ro = np.zeros(nt + 1, np.uint32)
+    runs = np.zeros((max(nr, 1), 2), np.uint32)
+    co = np.zeros(nt + 1, np.uint32)
+    fl = np.zeros(max(nc, 1), np.uint16)
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(L.clear_tile_map_build(grid_h, grid_w, r2, tile_h, tile_w, sub_h, sub_w, chunk,
+                                  ro.ctypes.data, runs.ctypes.data, nr, co.ctypes.data,
+                                  fl.ctypes.data, nc, ctypes.byref(a), ctypes.byref(b)))
+    return {"run_offsets": ro, "runs": runs[:nr], "chunk_offsets": co, "flags": fl[:nc]}
+
+
+def tile_map_build_device(grid_h, grid_w, r2, tile_h=TILE_H, tile_w=TILE_W, sub_h=SUB_H,
+                          sub_w=SUB_W, chunk=CHUNK, device="cuda"):
+    """Device-built tile map; returns numpy copies of the device arrays."""
+    import torch
+
+    L = lib()
+    nr, nc = tile_map_size(grid_h, grid_w, r2, tile_h, tile_w, sub_h, sub_w, chunk)
+    nt = _ntiles(grid_h, grid_w, tile_h, tile_w)
+    ro = torch.zeros(nt + 1, dtype=torch.int32, device=device)
+    runs = torch.zeros(max(nr, 1) * 2, dtype=torch.int32, device=device)
+    co = torch.zeros(nt + 1, dtype=torch.int32, device=device)
+    fl = torch.zeros(max(nc, 1), dtype=torch.int16, device=device)
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(L.clear_tile_map_build_device(grid_h, grid_w, r2, tile_h, tile_w, sub_h, sub_w, chunk,
+                                         ro.data_ptr(), runs.data_ptr(), nr, co.data_ptr(),
+                                         fl.data_ptr(), nc, ctypes.byref(a), ctypes.byref(b),
+                                         _stream_of(ro)))
+    torch.cuda.current_stream(ro.device).synchronize()
+    return {
+        "run_offsets": ro.cpu().numpy().view(np.uint32),
+        "runs": runs.cpu().numpy().view(np.uint32).reshape(-1, 2)[:nr],
+        "chunk_offsets": co.cpu().numpy().view(np.uint32),
+        "flags": fl.cpu().numpy().view(np.uint16)[:nc],
+    }

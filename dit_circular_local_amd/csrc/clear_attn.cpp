@@ -1,0 +1,270 @@
+// clear_attn.cpp -- C ABI of libclear_attn.so: argument checks, tile-map cache,
+// text-row workspace and launch sequencing.  See include/clear_attn.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include "clear_internal.h"
+
+namespace clear {
+
+namespace {
+thread_local char g_err[512];
+
+struct TileMapDev {
+  void* block = nullptr;  // one allocation holding the four arrays
+  uint32_t* run_off = nullptr;
+  uint32_t* runs = nullptr;
+  uint32_t* chunk_off = nullptr;
+  uint16_t* flags = nullptr;
+  size_t n_runs = 0, n_chunks = 0;
+  hipEvent_t ready = nullptr;  // recorded after the build kernels
+};
+
+struct DevState {
+  std::map<std::tuple<int, int, int>, TileMapDev> maps;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+};
+
+std::mutex g_mu;
+std::map<int, DevState> g_dev;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int hip_fail(hipError_t e, const char* what) {
+  return set_error(CLEAR_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Tile map of the kernels' fixed tiling for (gh, gw, r2) on the current device;
+// built on `stream` on first use.  Caller holds g_mu.
+int get_tile_map(DevState& ds, int gh, int gw, int r2, hipStream_t stream, TileMapDev** out) {
+  TileGeom g = make_geom(gh, gw, r2, CLEAR_TILE_H, CLEAR_TILE_W, CLEAR_SUB_H, CLEAR_SUB_W, CLEAR_CHUNK);
+  auto key = std::make_tuple(gh, gw, g.r2);
+  auto it = ds.maps.find(key);
+  if (it != ds.maps.end()) {
+    *out = &it->second;
+    return CLEAR_OK;
+  }
+  TileMapDev m;
+  tile_map_counts(g, &m.n_runs, &m.n_chunks, nullptr, nullptr);
+  const size_t nt = (size_t)g.nty * g.ntx;
+  const size_t o_ro = 0;
+  const size_t o_runs = align_up(o_ro + (nt + 1) * 4, 256);
+  const size_t o_co = align_up(o_runs + m.n_runs * 8, 256);
+  const size_t o_fl = align_up(o_co + (nt + 1) * 4, 256);
+  const size_t bytes = align_up(o_fl + m.n_chunks * 2 + 2, 256);
+  hipError_t e = hipMalloc(&m.block, bytes);
+  if (e != hipSuccess) return set_error(CLEAR_ENOMEM, "tile map allocation (%zu bytes): %s", bytes, hipGetErrorString(e));
+  char* b = (char*)m.block;
+  m.run_off = (uint32_t*)(b + o_ro);
+  m.runs = (uint32_t*)(b + o_runs);
+  m.chunk_off = (uint32_t*)(b + o_co);
+  m.flags = (uint16_t*)(b + o_fl);
+  int rc = tile_map_build_device_launch(g, m.run_off, m.runs, m.chunk_off, m.flags, nullptr, stream);
+  if (rc) {
+    (void)hipFree(m.block);
+    return rc;
+  }
+  if ((e = hipEventCreateWithFlags(&m.ready, hipEventDisableTiming)) != hipSuccess ||
+      (e = hipEventRecord(m.ready, stream)) != hipSuccess) {
+    (void)hipStreamSynchronize(stream);
+    (void)hipFree(m.block);
+    return hip_fail(e, "tile map event");
+  }
+  auto ins = ds.maps.emplace(key, m);
+  *out = &ins.first->second;
+  return CLEAR_OK;
+}
+
+// Text-row split count: make a text workgroup's key range (its critical path)
+// at most about half of the ideal time of the whole launch.
+int choose_text_splits(int B, int H, int n_text, int N, int ntiles, size_t img_chunks) {
+  if (n_text == 0) return 1;
+  const double nall = (N + CLEAR_CHUNK - 1) / CLEAR_CHUNK;
+  const double text_blocks = (n_text + 127) / 128;
+  const double nt_ch = (n_text + CLEAR_CHUNK - 1) / CLEAR_CHUNK;
+  // wavefront-chunks of work (each = 32 queries x 32 keys)
+  const double w_img = (double)B * H * (4.0 * ntiles * nt_ch + 3.0 * (double)img_chunks);
+  const double w_text = (double)B * H * text_blocks * 4.0 * nall;
+  const double slots = 256.0 * 4.0 * 2.0;  // CUs x SIMDs x resident waves
+  const double t_ideal = (w_img + w_text) / slots;
+  int s = (int)(2.0 * nall / (t_ideal > 1.0 ? t_ideal : 1.0)) + 1;
+  int smax = (int)(nall / 8.0);
+  if (s > smax) s = smax;
+  if (s > 64) s = 64;
+  if (s < 1) s = 1;
+  return s;
+}
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+int set_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void clear_error_reset() { g_err[0] = 0; }
+
+bool debug_sync_enabled() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("CLEAR_DEBUG");
+    v = (e && e[0] == '1') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+}  // namespace clear
+
+using namespace clear;
+
+extern "C" const char* clear_last_error(void) { return g_err; }
+
+extern "C" int clear_version(void) { return 100; }
+
+extern "C" int clear_attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B,
+                                 int H, int d, int n_text, int grid_h, int grid_w,
+                                 const clear_opts* opts, void* stream) {
+  clear_error_reset();
+  clear_opts o = opts ? *opts : clear_opts{CLEAR_BF16, 0, nullptr, 0};
+  if (!q || !k || !v || !out) return set_error(CLEAR_EINVAL, "q, k, v and out must not be NULL");
+  if (B < 1 || H < 1) return set_error(CLEAR_EINVAL, "B and H must be >= 1 (got %d, %d)", B, H);
+  if (d != 64 && d != 128) return set_error(CLEAR_EINVAL, "d must be 64 or 128 (got %d)", d);
+  if (n_text < 0) return set_error(CLEAR_EINVAL, "n_text must be >= 0 (got %d)", n_text);
+  if (grid_h < 1 || grid_w < 1 || grid_h > CLEAR_MAX_GRID || grid_w > CLEAR_MAX_GRID)
+    return set_error(CLEAR_EINVAL, "grid sides must be in 1..%d (got %d x %d)", CLEAR_MAX_GRID, grid_h, grid_w);
+  if (o.dtype != CLEAR_BF16 && o.dtype != CLEAR_FP32)
+    return set_error(CLEAR_EINVAL, "dtype must be CLEAR_BF16 or CLEAR_FP32 (got %d)", o.dtype);
+  if (o.r2_max < -1) return set_error(CLEAR_EINVAL, "r2_max must be >= -1 (got %d)", o.r2_max);
+  if (n_text == 0 && o.r2_max < 0)
+    return set_error(CLEAR_EINVAL, "n_text == 0 and r2_max < 0: every query row would be empty");
+  if (o.text_splits < 0 || o.text_splits > 64)
+    return set_error(CLEAR_EINVAL, "text_splits must be in 0..64 (got %d)", o.text_splits);
+  const long long N = (long long)n_text + (long long)grid_h * grid_w;
+  if (N > 0x7fffffffLL) return set_error(CLEAR_EINVAL, "sequence too long");
+  const size_t elem = o.dtype == CLEAR_BF16 ? 2 : 4;
+  const size_t bytes = (size_t)B * H * (size_t)N * d * elem;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15)
+    return set_error(CLEAR_EINVAL, "q, k, v and out must be 16-byte aligned");
+  if (ranges_overlap(out, bytes, q, bytes) || ranges_overlap(out, bytes, k, bytes) ||
+      ranges_overlap(out, bytes, v, bytes))
+    return set_error(CLEAR_EINVAL, "out must not overlap q, k or v");
+  if (o.lse_out && ((uintptr_t)o.lse_out & 3)) return set_error(CLEAR_EINVAL, "lse_out must be 4-byte aligned");
+
+  hipStream_t s = (hipStream_t)stream;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+
+  std::lock_guard<std::mutex> lock(g_mu);
+  DevState& ds = g_dev[dev];
+  TileMapDev* tm = nullptr;
+  int rc = get_tile_map(ds, grid_h, grid_w, o.r2_max, s, &tm);
+  if (rc) return rc;
+  if ((e = hipStreamWaitEvent(s, tm->ready, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+
+  TileGeom g = make_geom(grid_h, grid_w, o.r2_max, CLEAR_TILE_H, CLEAR_TILE_W, CLEAR_SUB_H, CLEAR_SUB_W, CLEAR_CHUNK);
+  int splits = o.text_splits ? o.text_splits
+                             : choose_text_splits(B, H, n_text, (int)N, g.nty * g.ntx, tm->n_chunks);
+  AttnLaunch a;
+  memset(&a, 0, sizeof a);
+  a.q = q; a.k = k; a.v = v; a.out = out; a.lse = o.lse_out;
+  a.run_off = tm->run_off; a.runs = tm->runs; a.chunk_off = tm->chunk_off; a.flags = tm->flags;
+  a.B = B; a.H = H; a.d = d; a.n_text = n_text; a.gh = grid_h; a.gw = grid_w; a.r2 = g.r2;
+  a.dtype = o.dtype; a.text_splits = splits;
+  if (splits > 1 && n_text > 0) {
+    const size_t o_bytes = align_up((size_t)splits * B * H * n_text * d * 4, 256);
+    const size_t need = o_bytes + (size_t)splits * B * H * n_text * 2 * 4;
+    if (need > ds.ws_bytes) {
+      // the old workspace may still be read by queued kernels
+      if (ds.ws) {
+        if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+        (void)hipFree(ds.ws);
+        ds.ws = nullptr;
+        ds.ws_bytes = 0;
+      }
+      if ((e = hipMalloc(&ds.ws, need)) != hipSuccess)
+        return set_error(CLEAR_ENOMEM, "text workspace (%zu bytes): %s", need, hipGetErrorString(e));
+      ds.ws_bytes = need;
+    }
+    a.ws_o = (float*)ds.ws;
+    a.ws_ml = (float*)((char*)ds.ws + o_bytes);
+  }
+  rc = attn_launch(a, stream);
+  if (rc) return rc;
+  if (debug_sync_enabled()) {
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "CLEAR_DEBUG sync");
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "CLEAR_DEBUG check");
+  }
+  return CLEAR_OK;
+}
+
+extern "C" int clear_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H,
+                              int d, int n_text, int grid_h, int grid_w, int radius, void* stream) {
+  clear_error_reset();
+  if (radius < 0) return set_error(CLEAR_EINVAL, "radius must be >= 0 (got %d)", radius);
+  long long r2 = (long long)radius * radius;
+  if (r2 > 0x7fffffffLL) r2 = 0x7fffffffLL;
+  clear_opts o{CLEAR_BF16, (int)r2, nullptr, 0};
+  return clear_attn_fwd_ex(q, k, v, out, B, H, d, n_text, grid_h, grid_w, &o, stream);
+}
+
+extern "C" int clear_tile_map_build_device(int grid_h, int grid_w, int r2_max, int tile_h, int tile_w,
+                                           int sub_h, int sub_w, int chunk, uint32_t* run_offsets,
+                                           uint32_t* runs, size_t runs_cap, uint32_t* chunk_offsets,
+                                           uint16_t* flags, size_t flags_cap, size_t* n_runs,
+                                           size_t* n_chunks, void* stream) {
+  clear_error_reset();
+  int rc = tile_map_validate(grid_h, grid_w, r2_max, tile_h, tile_w, sub_h, sub_w, chunk);
+  if (rc) return rc;
+  if (!n_runs || !n_chunks) return set_error(CLEAR_EINVAL, "n_runs / n_chunks must not be NULL");
+  TileGeom g = make_geom(grid_h, grid_w, r2_max, tile_h, tile_w, sub_h, sub_w, chunk);
+  tile_map_counts(g, n_runs, n_chunks, nullptr, nullptr);
+  if (*n_runs > runs_cap || *n_chunks > flags_cap)
+    return set_error(CLEAR_ENOMEM, "tile map needs %zu runs and %zu chunks (caps %zu, %zu)", *n_runs,
+                     *n_chunks, runs_cap, flags_cap);
+  if (!run_offsets || !chunk_offsets || (*n_runs && !runs) || (*n_chunks && !flags))
+    return set_error(CLEAR_EINVAL, "tile map output pointers must not be NULL");
+  if ((size_t)g.nty * g.ntx > (size_t)0x7fffffff) return set_error(CLEAR_EINVAL, "too many tiles");
+  rc = tile_map_build_device_launch(g, run_offsets, runs, chunk_offsets, flags, nullptr, stream);
+  if (rc) return rc;
+  if (debug_sync_enabled()) {
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "CLEAR_DEBUG sync");
+  }
+  return CLEAR_OK;
+}
+
+extern "C" void clear_release_cache(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  for (auto& kv : g_dev) {
+    if (hipSetDevice(kv.first) != hipSuccess) continue;
+    (void)hipDeviceSynchronize();
+    for (auto& m : kv.second.maps) {
+      if (m.second.ready) (void)hipEventDestroy(m.second.ready);
+      (void)hipFree(m.second.block);
+    }
+    kv.second.maps.clear();
+    if (kv.second.ws) (void)hipFree(kv.second.ws);
+    kv.second.ws = nullptr;
+    kv.second.ws_bytes = 0;
+  }
+  (void)hipSetDevice(cur);
+}

@@ -202,7 +202,8 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_text: int,
             for b in range(B) for h in range(H)]
     if workers > 1 and len(jobs) > 1:
         import multiprocessing as mp
-        with mp.get_context("fork").Pool(min(workers, len(jobs))) as pool:
+        # fresh interpreters: the caller may hold a GPU context, which must not be forked
+        with mp.get_context("spawn").Pool(min(workers, len(jobs))) as pool:
             res = pool.map(_head_job, jobs)
     else:
         res = [_head_job(j) for j in jobs]

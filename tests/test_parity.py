@@ -1,0 +1,170 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bars: fp32 max-abs <= 1e-5, bf16 max-abs <= 2e-2 (inputs widened exactly, the
+GPU output widened, oracle in fp64).  One key wrongly admitted or dropped moves
+an output by ~1/(window size), far above 1e-5, so the fp32 cases (which run the
+same chunk lists, flags and masks as bf16, at d = 64 and 128) pin the masks;
+the bf16 cases at r <= 2 pin them for bf16 as well.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import dit_circular_local_amd as ca
+from dit_circular_local_amd.inputs import WORKLOADS, make_qkv, workload_qkv
+from oracle import attention, attention_rows, tile_map_bruteforce
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-5, "bf16": 2e-2}
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _run(q, k, v, n_text, gh, gw, r2, **kw):
+    out = ca.fwd(q, k, v, n_text, gh, gw, r2=r2, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check_full(dtype, B, H, n_text, gh, gw, d, r2, seed=0, q_mult=1.0, splits=0, lse=True):
+    q, k, v = make_qkv(B, H, n_text, gh, gw, d, dtype, seed, rms_norm=(dtype == "bf16"),
+                       scale=1.0 if dtype == "bf16" else 1.0 / math.sqrt(d), q_mult=q_mult,
+                       device="cuda")
+    out, l = _run(q, k, v, n_text, gh, gw, r2, return_lse=lse, text_splits=splits) if lse else \
+        (_run(q, k, v, n_text, gh, gw, r2, text_splits=splits), None)
+    ref, ref_lse = attention(_np(q), _np(k), _np(v), n_text, gh, gw, r2, workers=8)
+    err = np.abs(_np(out) - ref).max()
+    assert err <= TOL[dtype], f"{dtype} B{B} H{H} T{n_text} {gh}x{gw} d{d} r2={r2}: max-abs {err:.3e}"
+    if lse:
+        lerr = np.abs(_np(l) - ref_lse).max()
+        assert lerr <= 1e-4, f"lse max-abs {lerr:.3e}"
+    return err
+
+
+def test_tiny_config_fp32():
+    """16x16 grid + 8 text tokens, d 64, r 4, fp32: every output element."""
+    w = WORKLOADS["tiny"]
+    q, k, v = workload_qkv(w, seed=0, device="cuda")
+    out = _run(q, k, v, w.n_text, w.grid_h, w.grid_w, 16)
+    ref, _ = attention(_np(q), _np(k), _np(v), w.n_text, w.grid_h, w.grid_w, 16)
+    assert np.abs(_np(out) - ref).max() <= 1e-5
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n_text,gh,gw", [(8, 16, 16), (0, 19, 13), (1, 37, 19), (130, 24, 40)])
+@pytest.mark.parametrize("r2", [-1, 0, 1, 2, 4, 8, 24, 63, 64, 10 ** 6])
+def test_fp32_masks_exact(d, n_text, gh, gw, r2):
+    if n_text == 0 and r2 < 0:
+        pytest.skip("empty rows")
+    _check_full("fp32", 1, 2, n_text, gh, gw, d, r2)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n_text,gh,gw", [(8, 16, 16), (0, 21, 11), (33, 37, 19), (512, 20, 24)])
+@pytest.mark.parametrize("r2", [-1, 0, 1, 2, 5, 16, 63, 64, 10 ** 6])
+def test_bf16_small_grids(d, n_text, gh, gw, r2):
+    if n_text == 0 and r2 < 0:
+        pytest.skip("empty rows")
+    _check_full("bf16", 1, 2, n_text, gh, gw, d, r2)
+
+
+def test_radius_zero_without_text_is_exact_copy_of_v():
+    """r2 = 0, no text: each row admits only itself, so O = V exactly (bf16)."""
+    q, k, v = make_qkv(1, 3, 0, 23, 17, 128, "bf16", 5, device="cuda")
+    out = _run(q, k, v, 0, 23, 17, 0)
+    assert torch.equal(out, v)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 64])
+def test_text_splits_agree(splits):
+    _check_full("fp32", 1, 2, 150, 30, 30, 128, 49, splits=splits)
+
+
+def test_batch_and_heads_and_large_logits():
+    _check_full("bf16", 2, 3, 40, 33, 18, 128, 36)
+    # Q x 8: peaked softmax, exercises the running-max updates
+    _check_full("bf16", 1, 2, 64, 32, 32, 128, 64, q_mult=8.0)
+    _check_full("fp32", 1, 2, 64, 32, 32, 128, 64, q_mult=8.0)
+
+
+def test_strict_and_inclusive_conventions_differ_only_on_the_circle():
+    q, k, v = make_qkv(1, 1, 16, 40, 40, 128, "fp32", 3, rms_norm=False, scale=1 / 8, device="cuda")
+    for r in (4, 8):
+        for r2 in (r * r, r * r - 1):
+            out = _run(q, k, v, 16, 40, 40, r2)
+            ref, _ = attention(_np(q), _np(k), _np(v), 16, 40, 40, r2)
+            assert np.abs(_np(out) - ref).max() <= 1e-5
+
+
+@pytest.mark.parametrize("r", [8, 16, 32])
+def test_flux_1024_bf16_and_fp32(r):
+    """64x64 grid + 512 text, d 128: bf16 on 4 heads, fp32 (mask exactness) on 2 heads."""
+    _check_full("bf16", 1, 4, 512, 64, 64, 128, r * r, seed=1)
+    _check_full("fp32", 1, 2, 512, 64, 64, 128, r * r, seed=2)
+
+
+def test_default_entry_point_matches_ex():
+    q, k, v = make_qkv(1, 2, 512, 32, 32, 128, "bf16", 7, device="cuda")
+    a = ca.fwd(q, k, v, 512, 32, 32, radius=8, use_ex=False)
+    b = ca.fwd(q, k, v, 512, 32, 32, radius=8, use_ex=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_deterministic_repeats():
+    q, k, v = make_qkv(1, 4, 512, 64, 64, 128, "bf16", 11, device="cuda")
+    a = ca.fwd(q, k, v, 512, 64, 64, radius=16)
+    # poison a second output buffer first
+    b = torch.full_like(a, float("nan"))
+    ca.fwd(q, k, v, 512, 64, 64, radius=16, out=b)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("gh,gw,r2", [(64, 64, 64), (64, 64, 1023), (37, 19, 5), (512, 512, 1024),
+                                      (9, 40, -1), (128, 128, 10 ** 6)])
+def test_device_tile_map_matches_host(gh, gw, r2):
+    dev = ca.tile_map_build_device(gh, gw, r2)
+    host = ca.tile_map_build(gh, gw, r2)
+    for key in host:
+        np.testing.assert_array_equal(dev[key], host[key], err_msg=key)
+    if gh * gw <= 4096:
+        ref = tile_map_bruteforce(gh, gw, r2, box=True)
+        for key in ref:
+            np.testing.assert_array_equal(dev[key], ref[key], err_msg=key)
+
+
+def _sample_rows(n_text, g, rng, n_img=48, n_txt=6):
+    cells = [(0, 0), (0, g - 1), (g - 1, 0), (g - 1, g - 1), (15, 7), (16, 8), (g // 2, g // 2),
+             (31, 0), (0, 31), (g - 17, g - 9)]
+    cells += [tuple(x) for x in rng.integers(0, g, (n_img - len(cells), 2))]
+    rows = [n_text + y * g + x for y, x in cells]
+    rows += [0, n_text - 1] + rng.integers(0, n_text, n_txt - 2).tolist()
+    return sorted(set(rows))
+
+
+@pytest.mark.parametrize("r", [8, 32])
+def test_flux_8192_sampled_rows(r):
+    """512x512 grid + 512 text tokens, 24 heads, bf16, the benchmark's launch
+    configuration: sampled rows of two heads against the oracle row by row."""
+    w = WORKLOADS["flux8k"]
+    q, k, v = workload_qkv(w, seed=0, device="cuda")
+    out = ca.fwd(q, k, v, w.n_text, w.grid_h, w.grid_w, radius=r)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(r)
+    for h in (0, 23):
+        rows = _sample_rows(w.n_text, w.grid_h, rng)
+        ref, _ = attention_rows(_np(q[0, h]), _np(k[0, h]), _np(v[0, h]), w.n_text, w.grid_h,
+                                w.grid_w, r * r, rows)
+        got = _np(out[0, h, rows])
+        err = np.abs(got - ref).max()
+        assert err <= 2e-2, f"head {h}: max-abs {err:.3e}"
+    assert torch.isfinite(out).all()
+    del q, k, v, out
+    torch.cuda.empty_cache()

@@ -1,0 +1,61 @@
+"""The library's host tile-map builder against the oracle's brute force, bit for bit."""
+
+import numpy as np
+import pytest
+
+import dit_circular_local_amd as ca
+from oracle import tile_map_bruteforce
+
+
+def _same(lib_tm, ref):
+    for key in ("run_offsets", "runs", "chunk_offsets", "flags"):
+        np.testing.assert_array_equal(lib_tm[key], ref[key], err_msg=key)
+
+
+def _radii(gh, gw):
+    diag2 = (gh - 1) ** 2 + (gw - 1) ** 2
+    out = []
+    for r in (0, 1, 2, 3, 4, 8, 16, 32):
+        out += [r * r, max(r * r - 1, -1)]
+    return sorted(set(out + [-1, 2, 5, diag2, diag2 + 7]))
+
+
+@pytest.mark.parametrize("gh,gw", [(1, 1), (1, 9), (7, 1), (5, 5), (16, 8), (17, 9), (13, 30), (33, 24)])
+def test_small_grids_all_radii_both_conventions(gh, gw):
+    for r2 in _radii(gh, gw):
+        _same(ca.tile_map_build(gh, gw, r2), tile_map_bruteforce(gh, gw, r2))
+
+
+@pytest.mark.parametrize("tiling", [(4, 4, 2, 4, 8), (8, 8, 4, 4, 16), (2, 2, 1, 2, 4), (1, 1, 1, 1, 1),
+                                    (16, 16, 8, 8, 64), (6, 9, 3, 3, 7)])
+def test_other_tilings(tiling):
+    th, tw, sh, sw, c = tiling
+    for gh, gw, r2 in [(11, 13, 5), (20, 7, 17), (9, 9, 0), (12, 12, 200)]:
+        _same(ca.tile_map_build(gh, gw, r2, th, tw, sh, sw, c),
+              tile_map_bruteforce(gh, gw, r2, th, tw, sh, sw, c))
+
+
+@pytest.mark.parametrize("r", [8, 16, 32])
+def test_flux_1024_grid_every_tile(r):
+    """64 x 64 token grid (1024^2 image), the kernels' tiling, both conventions."""
+    for r2 in (r * r, r * r - 1):
+        _same(ca.tile_map_build(64, 64, r2), tile_map_bruteforce(64, 64, r2, box=True))
+
+
+@pytest.mark.parametrize("g,r", [(512, 8), (512, 32), (256, 16), (128, 32)])
+def test_large_grids_sampled_tiles(g, r):
+    """8192^2 .. 2048^2 grids: sampled tiles (corners, edges, interior) bit for bit."""
+    tm = ca.tile_map_build(g, g, r * r)
+    ntx = g // 8
+    nt = (g // 16) * ntx
+    rng = np.random.default_rng(r)
+    tiles = sorted(set([0, ntx - 1, nt - ntx, nt - 1, ntx + 1, nt // 2 + ntx // 2]
+                       + rng.integers(0, nt, 6).tolist()))
+    ref = tile_map_bruteforce(g, g, r * r, tiles=tiles, box=True)
+    for i, t in enumerate(tiles):
+        a, b = tm["run_offsets"][t], tm["run_offsets"][t + 1]
+        ra, rb = ref["run_offsets"][i], ref["run_offsets"][i + 1]
+        np.testing.assert_array_equal(tm["runs"][a:b], ref["runs"][ra:rb])
+        a, b = tm["chunk_offsets"][t], tm["chunk_offsets"][t + 1]
+        ra, rb = ref["chunk_offsets"][i], ref["chunk_offsets"][i + 1]
+        np.testing.assert_array_equal(tm["flags"][a:b], ref["flags"][ra:rb])

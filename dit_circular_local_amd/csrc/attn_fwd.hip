@@ -451,7 +451,10 @@ __global__ void __launch_bounds__(kThreads) clear_attn_fwd_kernel(Params p) {
       for (int a = 0; a < 4; ++a) {
         u32x4_t c4 = cp[2 * a + g];  // positions 8a + 4g .. 8a + 4g + 3
         for (int b = 0; b < 4; ++b) {
-          s16x2_t kc = __builtin_bit_cast(s16x2_t, c4[b]);
+          // (built from shifts: a bit_cast of the vector element itself was
+          // compiled as element 0 for every b)
+          const unsigned cv = c4[b];
+          const s16x2_t kc = {(short)(cv & 0xffffu), (short)(cv >> 16)};
           s16x2_t dd = qc - kc;
           int d2 = __builtin_amdgcn_sdot2(dd, dd, 0, false);
           if (d2 > p.r2) s[4 * a + b] = -__builtin_inff();

@@ -22,8 +22,14 @@
 //    O^T[d][query]  += V^T[d][key] . P^T[key][query]    A = V^T (LDS), B = P^T (VGPRs)
 // With the 32x32 accumulator layout, lane l holds 16 keys of query l % 32, so
 // the softmax row statistics are per lane (plus one exchange with lane l ^ 32)
-// and the rescaling of O^T is per lane.  bf16 uses v_mfma_f32_32x32x16_bf16,
-// fp32 uses v_mfma_f32_32x32x2_f32.
+// and the rescaling of O^T is per lane.  bf16 uses v_mfma_f32_32x32x16_bf16 with
+// V^T read from row-major V by the LDS transpose load ds_read_b64_tr_b16; fp32
+// uses v_mfma_f32_32x32x2_f32.
+//
+// Pipeline: three LDS stages and two register sets.  Chunk c is fetched from
+// global memory into register set c % 2 two iterations before it is used,
+// written to LDS stage c % 3 one iteration before, and consumed at iteration c;
+// one workgroup barrier per chunk.
 //
 // Online softmax in base 2 with a lazily updated reference max: p = 2^(s*c - M)
 // with c = log2(e)/sqrt(d); M is raised only when a row max exceeds M + 8, so
@@ -42,6 +48,10 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 typedef __attribute__((ext_vector_type(2))) short s16x2_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((ext_vector_type(8))) short s16x8_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
@@ -49,6 +59,8 @@ constexpr int kTileH = CLEAR_TILE_H;
 constexpr int kTileW = CLEAR_TILE_W;
 constexpr int kSubH = CLEAR_SUB_H;
 constexpr int kChunk = CLEAR_CHUNK;
+constexpr int kStages = 3;
+constexpr int kMaxLdsRuns = 256;     // tiles with more key rows fall back to global run reads
 constexpr int kTextQ = kWaves * 32;  // text queries per workgroup
 constexpr float kLazyTau = 8.0f;
 constexpr float kMInit = -1.0e30f;
@@ -81,39 +93,39 @@ struct Params {
 // index of the 32x32 accumulator layout.
 __device__ __forceinline__ int acc_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
 
+// Wave-wide combine of a value with its partner lane l ^ 32.
+__device__ __forceinline__ float max_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---------------------------------------------------------------- engines
 
-// bf16 inputs; K row-major and V transposed ([d][key]) in LDS.
+// bf16 inputs; K and V row-major in LDS (different row pitches: K is read
+// row-per-lane by ds_read_b128, V by 16-lane transpose loads).
 template <int D>
 struct Bf16 {
-  using T = unsigned short;
   static constexpr int kElem = 2;
-  static constexpr int kPPR = D / 8;             // 16-byte pieces per row
-  static constexpr int kKRow = D * 2 + 16;       // LDS bytes per K row
-  static constexpr int kVtRow = kChunk * 2 + 16; // LDS bytes per V^T row (one d)
+  static constexpr int kRowBytes = D * 2;       // global row
+  static constexpr int kPPR = D / 8;            // 16-byte pieces per row
+  static constexpr int kRowK = D * 2 + 16;
+  static constexpr int kRowV = D * 2 + 64;
   static constexpr int kKOff = 0;
-  static constexpr int kVOff = kChunk * kKRow;
-  static constexpr int kCOff = kVOff + D * kVtRow;
-  static constexpr int kStage = kCOff + kChunk * 4;
+  static constexpr int kVOff = kChunk * kRowK;
+  static constexpr int kCOff = kVOff + kChunk * kRowV;
+  static constexpr int kFOff = kCOff + kChunk * 4;
+  static constexpr int kStage = kFOff + 16;
   static constexpr int kKIters = kChunk * kPPR / kThreads;
-  static constexpr int kVUnits = (kChunk / 2) * kPPR;   // (key pair, piece) units
   static constexpr int kKK = D / 16;
   static constexpr int kNB = D / 32;
-  static_assert(kChunk * kPPR % kThreads == 0, "K pieces must split evenly");
+  static_assert(kChunk * kPPR % kThreads == 0, "pieces must split evenly");
 
   bf16x8_t q[kKK];
   f32x16_t o[kNB];
-  u32x4_t kreg[kKIters];
-  u32x4_t vreg[2];
-
-  __device__ static int kpos(int r) { return (threadIdx.x + r * kThreads) / kPPR; }
-  __device__ static int kcol(int r) { return (threadIdx.x + r * kThreads) % kPPR; }
-  __device__ static bool vact() { return threadIdx.x < kVUnits; }
-  __device__ static int vpair() { return threadIdx.x % (kChunk / 2); }
-  __device__ static int vcol() { return threadIdx.x / (kChunk / 2); }
-  // V^T column of key position p: swaps bits 2 and 3 so that the 8 keys one
-  // lane group feeds to a P.V step are 16 contiguous bytes.
-  __device__ static int vt_col(int p) { return (p & ~15) | ((p & 4) << 1) | ((p & 8) >> 1) | (p & 3); }
 
   __device__ void load_q(const char* qrow, bool valid, int g) {
     for (int kk = 0; kk < kKK; ++kk) {
@@ -124,40 +136,28 @@ struct Bf16 {
   __device__ void zero_o() {
     for (int nb = 0; nb < kNB; ++nb) o[nb] = f32x16_t{};
   }
-  // Global -> registers.  tok_k[r]: token of K piece r; tok_v[0..1]: tokens of the V pair.
-  __device__ void gload(const char* kbase, const char* vbase, const int* tok_k, const int* tok_v) {
-    for (int r = 0; r < kKIters; ++r)
-      kreg[r] = *(const u32x4_t*)(kbase + (size_t)tok_k[r] * (D * 2) + kcol(r) * 16);
-    if (vact()) {
-      vreg[0] = *(const u32x4_t*)(vbase + (size_t)tok_v[0] * (D * 2) + vcol() * 16);
-      vreg[1] = *(const u32x4_t*)(vbase + (size_t)tok_v[1] * (D * 2) + vcol() * 16);
-    }
-  }
-  // Registers -> LDS stage.
-  __device__ void lstore(char* st) {
-    for (int r = 0; r < kKIters; ++r)
-      *(u32x4_t*)(st + kKOff + kpos(r) * kKRow + kcol(r) * 16) = kreg[r];
-    if (vact()) {
-      char* vt = st + kVOff + vt_col(2 * vpair()) * 2;
-      int d0 = vcol() * 8;
-      for (int e = 0; e < 8; ++e) {
-        unsigned a = vreg[0][e >> 1], b = vreg[1][e >> 1];
-        unsigned w = (e & 1) ? __builtin_amdgcn_perm(b, a, 0x07060302u)
-                             : __builtin_amdgcn_perm(b, a, 0x05040100u);
-        *(unsigned*)(vt + (d0 + e) * kVtRow) = w;
-      }
-    }
-  }
   __device__ void qk(const char* st, int lane, f32x16_t& s) const {
-    const char* kb = st + kKOff + (lane & 31) * kKRow + (lane >> 5) * 16;
+    const char* kb = st + kKOff + (lane & 31) * kRowK + (lane >> 5) * 16;
     s = f32x16_t{};
     for (int kk = 0; kk < kKK; ++kk) {
       bf16x8_t a = *(const bf16x8_t*)(kb + kk * 32);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q[kk], s, 0, 0, 0);
     }
   }
+  // O^T += V^T P^T.  The A operand (lane l: d = 32*nb + l % 32, eight keys of
+  // lane group g = l / 32) comes from two transpose loads: in each 16-lane group,
+  // lane i receives element i % 4 of the 8-byte rows addressed by lanes i/4,
+  // i/4 + 4, i/4 + 8, i/4 + 12.  Lane s of a group therefore addresses key row
+  // 16t + 8h + 4g + s/4 (h = 0, 1 for the two loads) at columns
+  // 32nb + 16*((l/16) % 2) + 4*(s % 4): lane i then holds keys
+  // 16t + 8h + 4g + e (e = 0..3) at d = 32nb + l % 32, which are the keys of
+  // accumulator registers 8t + 4h + e (acc_row) whose probabilities the B
+  // operand carries.
   __device__ void pv(const char* st, int lane, const f32x16_t& p) {
     const int g = lane >> 5;
+    const int s = lane & 15;
+    const int half = (lane >> 4) & 1;
+    const char* vb = st + kVOff + (4 * g + (s >> 2)) * kRowV + (16 * half + 4 * (s & 3)) * 2;
     for (int t = 0; t < 2; ++t) {
       bf16x8_t b;
       for (int j = 0; j < 4; ++j) {
@@ -165,14 +165,16 @@ struct Bf16 {
         b[2 * j] = h[0];
         b[2 * j + 1] = h[1];
       }
-      const char* vb = st + kVOff + (lane & 31) * kVtRow + (16 * t + 8 * g) * 2;
       for (int nb = 0; nb < kNB; ++nb) {
-        bf16x8_t a = *(const bf16x8_t*)(vb + nb * 32 * kVtRow);
-        o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, o[nb], 0, 0, 0);
+        const char* a0 = vb + 16 * t * kRowV + nb * 64;
+        s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds_char_t*)const_cast<char*>(a0));
+        s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(lds_char_t*)const_cast<char*>(a0 + 8 * kRowV));
+        s16x8_t w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), b, o[nb], 0, 0, 0);
       }
     }
   }
-  // Store 4 consecutive output values (d0 .. d0+3) of one row.
   __device__ static void store4(char* dst, float a, float b, float c, float d) {
     bf16x2_t h0 = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
     bf16x2_t h1 = __builtin_convertvector(f32x2_t{c, d}, bf16x2_t);
@@ -186,14 +188,16 @@ struct Bf16 {
 // fp32 inputs; K and V row-major in LDS.
 template <int D>
 struct F32 {
-  using T = float;
   static constexpr int kElem = 4;
+  static constexpr int kRowBytes = D * 4;
   static constexpr int kPPR = D / 4;
-  static constexpr int kRow = D * 4 + 16;
+  static constexpr int kRowK = D * 4 + 16;
+  static constexpr int kRowV = D * 4 + 16;
   static constexpr int kKOff = 0;
-  static constexpr int kVOff = kChunk * kRow;
-  static constexpr int kCOff = 2 * kChunk * kRow;
-  static constexpr int kStage = kCOff + kChunk * 4;
+  static constexpr int kVOff = kChunk * kRowK;
+  static constexpr int kCOff = kVOff + kChunk * kRowV;
+  static constexpr int kFOff = kCOff + kChunk * 4;
+  static constexpr int kStage = kFOff + 16;
   static constexpr int kKIters = kChunk * kPPR / kThreads;
   static constexpr int kHalf = D / 2;   // d values per lane group in Q.K
   static constexpr int kNB = D / 32;
@@ -201,11 +205,6 @@ struct F32 {
 
   float q[kHalf];
   f32x16_t o[kNB];
-  u32x4_t kreg[kKIters];
-  u32x4_t vreg[kKIters];
-
-  __device__ static int kpos(int r) { return (threadIdx.x + r * kThreads) / kPPR; }
-  __device__ static int kcol(int r) { return (threadIdx.x + r * kThreads) % kPPR; }
 
   __device__ void load_q(const char* qrow, bool valid, int g) {
     for (int s4 = 0; s4 < kHalf / 4; ++s4) {
@@ -216,20 +215,8 @@ struct F32 {
   __device__ void zero_o() {
     for (int nb = 0; nb < kNB; ++nb) o[nb] = f32x16_t{};
   }
-  __device__ void gload(const char* kbase, const char* vbase, const int* tok_k, const int* tok_v) {
-    for (int r = 0; r < kKIters; ++r) {
-      kreg[r] = *(const u32x4_t*)(kbase + (size_t)tok_k[r] * (D * 4) + kcol(r) * 16);
-      vreg[r] = *(const u32x4_t*)(vbase + (size_t)tok_v[r] * (D * 4) + kcol(r) * 16);
-    }
-  }
-  __device__ void lstore(char* st) {
-    for (int r = 0; r < kKIters; ++r) {
-      *(u32x4_t*)(st + kKOff + kpos(r) * kRow + kcol(r) * 16) = kreg[r];
-      *(u32x4_t*)(st + kVOff + kpos(r) * kRow + kcol(r) * 16) = vreg[r];
-    }
-  }
   __device__ void qk(const char* st, int lane, f32x16_t& s) const {
-    const char* kb = st + kKOff + (lane & 31) * kRow + (lane >> 5) * kHalf * 4;
+    const char* kb = st + kKOff + (lane & 31) * kRowK + (lane >> 5) * kHalf * 4;
     s = f32x16_t{};
     for (int s4 = 0; s4 < kHalf / 4; ++s4) {
       f32x4_t a = *(const f32x4_t*)(kb + s4 * 16);
@@ -240,7 +227,7 @@ struct F32 {
   __device__ void pv(const char* st, int lane, const f32x16_t& p) {
     const int g = lane >> 5;
     for (int u = 0; u < 16; ++u) {
-      const float* vr = (const float*)(st + kVOff + acc_row(u, g) * kRow) + (lane & 31);
+      const float* vr = (const float*)(st + kVOff + acc_row(u, g) * kRowV) + (lane & 31);
       for (int nb = 0; nb < kNB; ++nb)
         o[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[32 * nb], p[u], o[nb], 0, 0, 0);
     }
@@ -252,87 +239,182 @@ struct F32 {
 
 // ---------------------------------------------------------------- key sources
 
-// Token and validity of key position p of chunk j for the current workgroup.
+// Maps (chunk j, position p) to a key token for the current workgroup.
+// Chunks 0 .. n_dense-1 are a dense token range (the text keys of an image
+// tile, or a key range of a text workgroup); the rest walk the tile's runs.
 struct KeySource {
-  // dense range: tokens base .. limit-1 (text chunks, text rows)
-  int dense_base;   // token of chunk 0 position 0
-  int dense_limit;  // first invalid token
-  int n_dense;      // number of dense chunks
-  // image runs of the tile
-  const uint32_t* runs;
-  int r_begin, r_end;   // absolute run indices
-  uint32_t total;       // keys in the tile's list
-  int n_text;
-  int gw;
-  // cursor: run containing the first position of the next image chunk to load
-  int cur_i;
-  uint32_t cur_base;
+  int dense_base, dense_limit, n_dense;
+  int n_text, gw;
+  uint32_t total;          // keys in the tile's list
+  int nr;                  // runs of the tile
+  bool lds;                // runs cached in LDS (flat offsets and packed start cells)
+  const uint32_t* g_runs;  // the tile's runs in global memory (start, length)
+  const uint32_t* l_off;   // LDS [nr + 1] flat offset of each run
+  const uint32_t* l_pos;   // LDS [nr] (ky << 16) | kx of each run's first key
+  int cur;                 // run containing the first position of the current chunk
+  uint32_t cur_base;       // its flat offset (global path)
 
-  __device__ uint32_t rlen(int i) const { return runs[2 * i + 1]; }
-  __device__ uint32_t rstart(int i) const { return runs[2 * i]; }
-
-  // Token for position p of chunk j (j < n_dense: dense, else image chunk j - n_dense).
-  // Out-of-range positions return a clamped, in-bounds token and valid = false.
+  // Move the cursor to flat position f0 (non-decreasing across calls).
+  __device__ void seek(uint32_t f0) {
+    if (lds) {
+      while (cur + 1 < nr && l_off[cur + 1] <= f0) ++cur;
+    } else {
+      while (cur + 1 < nr && cur_base + g_runs[2 * cur + 1] <= f0) {
+        cur_base += g_runs[2 * cur + 1];
+        ++cur;
+      }
+    }
+  }
+  // Token of position p of chunk j; out-of-range positions return a clamped,
+  // in-bounds token with valid = false.  (ky, kx) are the key's grid cell.
   __device__ int token(int j, int p, bool& valid, int& ky, int& kx) const {
     if (j < n_dense) {
       int t = dense_base + j * kChunk + p;
       valid = t < dense_limit;
-      ky = 0; kx = 0;
+      ky = 0;
+      kx = 0;
       return valid ? t : dense_limit - 1;
     }
     uint32_t f = (uint32_t)(j - n_dense) * kChunk + p;
     valid = f < total;
     if (!valid) f = total - 1;
-    int i = cur_i;
-    uint32_t b = cur_base;
-    while (i + 1 < r_end && f >= b + rlen(i)) {
-      b += rlen(i);
-      ++i;
+    if (lds) {
+      int i = cur;
+      while (i + 1 < nr && l_off[i + 1] <= f) ++i;
+      const uint32_t pos = l_pos[i];
+      ky = (int)(pos >> 16);
+      kx = (int)(pos & 0xffffu) + (int)(f - l_off[i]);
+    } else {
+      int i = cur;
+      uint32_t b = cur_base;
+      while (i + 1 < nr && f >= b + g_runs[2 * i + 1]) {
+        b += g_runs[2 * i + 1];
+        ++i;
+      }
+      const uint32_t s = g_runs[2 * i];
+      ky = (int)(s / (uint32_t)gw);
+      kx = (int)(s - (uint32_t)ky * (uint32_t)gw) + (int)(f - b);
     }
-    uint32_t s = rstart(i) + (f - b);
-    ky = (int)(rstart(i) / (uint32_t)gw);
-    kx = (int)(s - (uint32_t)ky * (uint32_t)gw);
-    return n_text + (int)s;
-  }
-  // Move the cursor to the first position of image chunk (j + 1 - n_dense).
-  __device__ void advance_past(int j) {
-    if (j < n_dense - 1) return;
-    uint32_t f = (uint32_t)(j + 1 - n_dense) * kChunk;
-    while (cur_i + 1 < r_end && cur_base + rlen(cur_i) <= f) {
-      cur_base += rlen(cur_i);
-      ++cur_i;
-    }
+    return n_text + ky * gw + kx;
   }
 };
 
-// ---------------------------------------------------------------- kernel
+// One chunk in flight in registers: K and V pieces, packed key cells, chunk flags.
+template <class E>
+struct RegSet {
+  u32x4_t k[E::kKIters];
+  u32x4_t v[E::kKIters];
+  unsigned c[E::kKIters];
+  unsigned flag;
+};
+
+__device__ __forceinline__ int kpos_of(int r, int ppr) { return (threadIdx.x + r * kThreads) / ppr; }
+__device__ __forceinline__ int kcol_of(int r, int ppr) { return (threadIdx.x + r * kThreads) % ppr; }
 
 template <class E>
-__device__ __forceinline__ void gather_chunk(E& eng, const KeySource& ks, int j, const char* kbase,
-                                             const char* vbase, unsigned& creg) {
-  int tok_k[E::kKIters > 2 ? E::kKIters : 2];
-  int tok_v[E::kKIters > 2 ? E::kKIters : 2];
-  bool valid;
-  int ky, kx;
-  for (int r = 0; r < E::kKIters; ++r) tok_k[r] = ks.token(j, E::kpos(r), valid, ky, kx);
-  if constexpr (sizeof(typename E::T) == 2) {
-    tok_v[0] = ks.token(j, 2 * E::vpair(), valid, ky, kx);
-    tok_v[1] = ks.token(j, 2 * E::vpair() + 1, valid, ky, kx);
+__device__ __forceinline__ void gather(RegSet<E>& rs, KeySource& ks, int j, const char* kbase,
+                                       const char* vbase, const uint16_t* flags, int co) {
+  if (j >= ks.n_dense) {
+    ks.seek((uint32_t)(j - ks.n_dense) * kChunk);
+    rs.flag = flags[co + (j - ks.n_dense)];
   } else {
-    for (int r = 0; r < E::kKIters; ++r) tok_v[r] = tok_k[r];
+    rs.flag = 0;
   }
-  eng.gload(kbase, vbase, tok_k, tok_v);
-  if (threadIdx.x < kChunk) {
-    ks.token(j, threadIdx.x, valid, ky, kx);
-    short cy = valid ? (short)ky : kCoordFar;
-    short cx = valid ? (short)kx : (short)0;
-    creg = (unsigned)(unsigned short)cx | ((unsigned)(unsigned short)cy << 16);
+  for (int r = 0; r < E::kKIters; ++r) {
+    bool valid;
+    int ky, kx;
+    const int tok = ks.token(j, kpos_of(r, E::kPPR), valid, ky, kx);
+    const size_t off = (size_t)tok * E::kRowBytes + kcol_of(r, E::kPPR) * 16;
+    rs.k[r] = *(const u32x4_t*)(kbase + off);
+    rs.v[r] = *(const u32x4_t*)(vbase + off);
+    const short cy = valid ? (short)ky : kCoordFar;
+    const short cx = valid ? (short)kx : (short)0;
+    rs.c[r] = (unsigned)(unsigned short)cx | ((unsigned)(unsigned short)cy << 16);
   }
 }
 
 template <class E>
-__global__ void __launch_bounds__(kThreads) clear_attn_fwd_kernel(Params p) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * E::kStage];
+__device__ __forceinline__ void lstore(char* st, const RegSet<E>& rs) {
+  for (int r = 0; r < E::kKIters; ++r) {
+    const int pos = kpos_of(r, E::kPPR), col = kcol_of(r, E::kPPR);
+    *(u32x4_t*)(st + E::kKOff + pos * E::kRowK + col * 16) = rs.k[r];
+    *(u32x4_t*)(st + E::kVOff + pos * E::kRowV + col * 16) = rs.v[r];
+    if (col == 0) *(unsigned*)(st + E::kCOff + pos * 4) = rs.c[r];
+  }
+  if (threadIdx.x == 0) *(unsigned*)(st + E::kFOff) = rs.flag;
+}
+
+struct SoftmaxState {
+  float M, L;
+};
+
+// Consume one chunk from LDS stage `st` (one wavefront).
+template <class E>
+__device__ __forceinline__ void compute_chunk(E& eng, SoftmaxState& sm, const char* st, int j,
+                                              const KeySource& ks, int lane, int wave,
+                                              s16x2_t qc, int r2, float scale_log2) {
+  const int g = lane >> 5;
+  int tail = 32;  // dense chunk: positions >= tail are masked
+  bool coord_mask = false;
+  if (j < ks.n_dense) {
+    const int rem_keys = ks.dense_limit - (ks.dense_base + j * kChunk);
+    tail = rem_keys < 32 ? rem_keys : 32;
+  } else {
+    const unsigned f = *(const unsigned*)(st + E::kFOff);
+    if (!((f >> wave) & 1u)) return;
+    coord_mask = !((f >> (8 + wave)) & 1u);
+  }
+
+  f32x16_t s;
+  eng.qk(st, lane, s);
+
+  if (tail < 32) {
+    for (int i = 0; i < 16; ++i)
+      if (acc_row(i, g) >= tail) s[i] = -__builtin_inff();
+  } else if (coord_mask) {
+    const u32x4_t* cp = (const u32x4_t*)(st + E::kCOff);
+    for (int a = 0; a < 4; ++a) {
+      const u32x4_t c4 = cp[2 * a + g];  // positions 8a + 4g .. 8a + 4g + 3
+      for (int b = 0; b < 4; ++b) {
+        // (built from shifts: a bit_cast of the vector element itself was
+        // compiled as element 0 for every b)
+        const unsigned cv = c4[b];
+        const s16x2_t kc = {(short)(cv & 0xffffu), (short)(cv >> 16)};
+        const s16x2_t dd = qc - kc;
+        const int d2 = __builtin_amdgcn_sdot2(dd, dd, 0, false);
+        if (d2 > r2) s[4 * a + b] = -__builtin_inff();
+      }
+    }
+  }
+
+  // online softmax (base 2, lazy reference max)
+  float mx = s[0];
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+  mx = max_xor32(mx);
+  const float mxs = mx * scale_log2;
+  if (__ballot(mxs > sm.M + kLazyTau) != 0ull) {
+    const float Mn = fmaxf(sm.M, mxs);
+    const float alpha = __builtin_amdgcn_exp2f(sm.M - Mn);
+    sm.L *= alpha;
+    for (int nb = 0; nb < E::kNB; ++nb)
+      for (int i = 0; i < 16; ++i) eng.o[nb][i] *= alpha;
+    sm.M = Mn;
+  }
+  float lsum = 0.0f;
+  for (int i = 0; i < 16; ++i) {
+    const float e = __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -sm.M));
+    s[i] = e;
+    lsum += e;
+  }
+  sm.L += lsum;
+  eng.pv(st, lane, s);
+}
+
+template <class E>
+__global__ void __launch_bounds__(kThreads, 2) clear_attn_fwd_kernel(Params p) {
+  __shared__ __attribute__((aligned(16))) char smem[kStages * E::kStage];
+  __shared__ uint32_t l_off[kMaxLdsRuns + 1];
+  __shared__ uint32_t l_pos[kMaxLdsRuns];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -346,27 +428,30 @@ __global__ void __launch_bounds__(kThreads) clear_attn_fwd_kernel(Params p) {
   int bh, qtok, qy = 0, qx = 0;
   bool qvalid;
   KeySource ks;
-  ks.runs = p.runs;
   ks.n_text = p.n_text;
   ks.gw = p.gw;
-  ks.cur_i = 0;
-  ks.cur_base = 0;
-  ks.r_begin = ks.r_end = 0;
   ks.total = 0;
+  ks.nr = 0;
+  ks.lds = true;
+  ks.g_runs = p.runs;
+  ks.l_off = l_off;
+  ks.l_pos = l_pos;
+  ks.cur = 0;
+  ks.cur_base = 0;
   int n_chunks;
   int split = 0, tq = 0;
-  int tile = 0, co = 0;
+  int co = 0;
   if (text_wg) {
     split = bid % p.splits;
-    int rest = bid / p.splits;
-    int tb = rest % p.n_text_blocks;
+    const int rest = bid / p.splits;
+    const int tb = rest % p.n_text_blocks;
     bh = rest / p.n_text_blocks;
     tq = tb * kTextQ + wave * 32 + qi;
     qvalid = tq < p.n_text;
     qtok = tq;
-    int c0 = split * p.chunks_per_split;
-    int nall = (p.N + kChunk - 1) / kChunk;
-    int c1 = c0 + p.chunks_per_split < nall ? c0 + p.chunks_per_split : nall;
+    const int c0 = split * p.chunks_per_split;
+    const int nall = (p.N + kChunk - 1) / kChunk;
+    const int c1 = c0 + p.chunks_per_split < nall ? c0 + p.chunks_per_split : nall;
     ks.dense_base = c0 * kChunk;
     ks.dense_limit = p.N;
     ks.n_dense = c1 - c0;
@@ -380,7 +465,7 @@ __global__ void __launch_bounds__(kThreads) clear_attn_fwd_kernel(Params p) {
     const int xcd = ib % 8, slot = ib / 8;
     const int logical = xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
     bh = logical / p.ntiles;
-    tile = logical - bh * p.ntiles;
+    const int tile = logical - bh * p.ntiles;
     const int ty = tile / p.ntx, tx = tile - (tile / p.ntx) * p.ntx;
     qy = ty * kTileH + wave * kSubH + (qi >> 3);
     qx = tx * kTileW + (qi & 7);
@@ -389,102 +474,82 @@ __global__ void __launch_bounds__(kThreads) clear_attn_fwd_kernel(Params p) {
     ks.dense_base = 0;
     ks.dense_limit = p.n_text;
     ks.n_dense = (p.n_text + kChunk - 1) / kChunk;
-    ks.r_begin = (int)p.run_off[tile];
-    ks.r_end = (int)p.run_off[tile + 1];
-    uint32_t tot = 0;
-    for (int i = ks.r_begin; i < ks.r_end; ++i) tot += p.runs[2 * i + 1];
-    ks.total = tot;
-    ks.cur_i = ks.r_begin;
+    const int r_begin = (int)p.run_off[tile];
+    const int nr = (int)p.run_off[tile + 1] - r_begin;
+    ks.nr = nr;
+    ks.g_runs = p.runs + 2 * (size_t)r_begin;
+    ks.lds = nr <= kMaxLdsRuns;
+    if (ks.lds) {
+      // runs -> LDS: packed first cell and an exclusive scan of the lengths
+      uint32_t len = 0;
+      if (tid < nr) {
+        const uint32_t s = ks.g_runs[2 * tid];
+        len = ks.g_runs[2 * tid + 1];
+        const uint32_t y = s / (uint32_t)p.gw;
+        l_pos[tid] = (y << 16) | (s - y * (uint32_t)p.gw);
+      }
+      l_off[tid + 1] = len;
+      if (tid == 0) l_off[0] = 0;
+      __syncthreads();
+      for (int d = 1; d < kMaxLdsRuns; d <<= 1) {
+        const uint32_t x = tid + 1 > d ? l_off[tid + 1 - d] : 0u;
+        __syncthreads();
+        l_off[tid + 1] += x;
+        __syncthreads();
+      }
+      ks.total = nr > 0 ? l_off[nr] : 0u;
+    } else {
+      uint32_t tot = 0;
+      for (int i = 0; i < nr; ++i) tot += ks.g_runs[2 * i + 1];
+      ks.total = tot;
+    }
     co = (int)p.chunk_off[tile];
     n_chunks = ks.n_dense + (int)(p.chunk_off[tile + 1] - p.chunk_off[tile]);
   }
 
-  const size_t head_off = (size_t)bh * p.N * (E::kPPR * 16);
+  const size_t head_off = (size_t)bh * p.N * E::kRowBytes;
   const char* kbase = p.k + head_off;
   const char* vbase = p.v + head_off;
 
   E eng;
-  eng.load_q(p.q + head_off + (size_t)(qvalid ? qtok : 0) * (E::kPPR * 16), qvalid, g);
+  eng.load_q(p.q + head_off + (size_t)(qvalid ? qtok : 0) * E::kRowBytes, qvalid, g);
   eng.zero_o();
   const bool wave_active = __ballot(qvalid) != 0ull;
   const s16x2_t qc = {(short)qx, (short)qy};
+  SoftmaxState sm{kMInit, 0.0f};
 
-  float M = kMInit, L = 0.0f;
-  unsigned creg = 0;
-
-  if (n_chunks > 0) {
-    gather_chunk(eng, ks, 0, kbase, vbase, creg);
-    ks.advance_past(0);
-  }
-  for (int j = 0; j < n_chunks; ++j) {
-    char* st = smem + (j & 1) * E::kStage;
-    eng.lstore(st);
-    if (tid < kChunk) *(unsigned*)(st + E::kCOff + tid * 4) = creg;
-    if (j + 1 < n_chunks) {
-      gather_chunk(eng, ks, j + 1, kbase, vbase, creg);
-      ks.advance_past(j + 1);
+  // ---- pipelined main loop: chunk c in register set c % 2, LDS stage c % 3
+  RegSet<E> s0, s1;
+  const int n = n_chunks;
+  if (n > 0) gather(s0, ks, 0, kbase, vbase, p.flags, co);
+  if (n > 1) gather(s1, ks, 1, kbase, vbase, p.flags, co);
+  if (n > 0) lstore(smem, s0);
+  if (n > 2) gather(s0, ks, 2, kbase, vbase, p.flags, co);
+  int st_cur = 0;  // stage of chunk j
+  for (int j = 0; j < n; j += 2) {
+    {
+      const int st_next = st_cur == kStages - 1 ? 0 : st_cur + 1;
+      if (j + 1 < n) lstore(smem + st_next * E::kStage, s1);
+      if (j + 3 < n) gather(s1, ks, j + 3, kbase, vbase, p.flags, co);
+      __syncthreads();
+      if (wave_active)
+        compute_chunk(eng, sm, smem + st_cur * E::kStage, j, ks, lane, wave, qc, p.r2, p.scale_log2);
+      st_cur = st_next;
     }
-    __syncthreads();
-
-    if (!wave_active) continue;
-    // What this wavefront does with chunk j.
-    bool dense = j < ks.n_dense;
-    int tail = 32;  // dense chunk: positions >= tail are masked
-    bool coord_mask = false;
-    if (dense) {
-      int rem_keys = ks.dense_limit - (ks.dense_base + j * kChunk);
-      tail = rem_keys < 32 ? rem_keys : 32;
-    } else {
-      unsigned f = p.flags[co + (j - ks.n_dense)];
-      if (!((f >> wave) & 1u)) continue;
-      coord_mask = !((f >> (8 + wave)) & 1u);
+    if (j + 1 < n) {
+      const int st_next = st_cur == kStages - 1 ? 0 : st_cur + 1;
+      if (j + 2 < n) lstore(smem + st_next * E::kStage, s0);
+      if (j + 4 < n) gather(s0, ks, j + 4, kbase, vbase, p.flags, co);
+      __syncthreads();
+      if (wave_active)
+        compute_chunk(eng, sm, smem + st_cur * E::kStage, j + 1, ks, lane, wave, qc, p.r2,
+                      p.scale_log2);
+      st_cur = st_next;
     }
-
-    f32x16_t s;
-    eng.qk(st, lane, s);
-
-    if (tail < 32) {
-      for (int i = 0; i < 16; ++i)
-        if (acc_row(i, g) >= tail) s[i] = -__builtin_inff();
-    } else if (coord_mask) {
-      const u32x4_t* cp = (const u32x4_t*)(st + E::kCOff);
-      for (int a = 0; a < 4; ++a) {
-        u32x4_t c4 = cp[2 * a + g];  // positions 8a + 4g .. 8a + 4g + 3
-        for (int b = 0; b < 4; ++b) {
-          // (built from shifts: a bit_cast of the vector element itself was
-          // compiled as element 0 for every b)
-          const unsigned cv = c4[b];
-          const s16x2_t kc = {(short)(cv & 0xffffu), (short)(cv >> 16)};
-          s16x2_t dd = qc - kc;
-          int d2 = __builtin_amdgcn_sdot2(dd, dd, 0, false);
-          if (d2 > p.r2) s[4 * a + b] = -__builtin_inff();
-        }
-      }
-    }
-
-    // online softmax (base 2, lazy reference max)
-    float mx = s[0];
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mxs = mx * p.scale_log2;
-    if (__ballot(mxs > M + kLazyTau) != 0ull) {
-      float Mn = fmaxf(M, mxs);
-      float alpha = __builtin_amdgcn_exp2f(M - Mn);
-      L *= alpha;
-      for (int nb = 0; nb < E::kNB; ++nb)
-        for (int i = 0; i < 16; ++i) eng.o[nb][i] *= alpha;
-      M = Mn;
-    }
-    for (int i = 0; i < 16; ++i) {
-      float e = __builtin_amdgcn_exp2f(fmaf(s[i], p.scale_log2, -M));
-      s[i] = e;
-      L += e;
-    }
-    eng.pv(st, lane, s);
   }
 
   // ---- epilogue
-  const float Lt = L + __shfl_xor(L, 32);
+  const float Lt = sum_xor32(sm.L);
   if (!qvalid) return;
   const int row = text_wg ? tq : qtok;
   if (text_wg && p.splits > 1) {
@@ -492,26 +557,26 @@ __global__ void __launch_bounds__(kThreads) clear_attn_fwd_kernel(Params p) {
     float* wo = p.ws_o + (((size_t)split * p.BH + bh) * p.n_text + tq) * (E::kNB * 32);
     for (int nb = 0; nb < E::kNB; ++nb)
       for (int a = 0; a < 4; ++a) {
-        int d0 = 32 * nb + 8 * a + 4 * g;
+        const int d0 = 32 * nb + 8 * a + 4 * g;
         *(f32x4_t*)(wo + d0) = f32x4_t{eng.o[nb][4 * a], eng.o[nb][4 * a + 1], eng.o[nb][4 * a + 2],
                                        eng.o[nb][4 * a + 3]};
       }
     if (g == 0) {
       float* wm = p.ws_ml + (((size_t)split * p.BH + bh) * p.n_text + tq) * 2;
-      wm[0] = M;
+      wm[0] = sm.M;
       wm[1] = Lt;
     }
     return;
   }
   const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
-  char* orow = p.out + head_off + (size_t)row * (E::kPPR * 16);
+  char* orow = p.out + head_off + (size_t)row * E::kRowBytes;
   for (int nb = 0; nb < E::kNB; ++nb)
     for (int a = 0; a < 4; ++a) {
-      int d0 = 32 * nb + 8 * a + 4 * g;
+      const int d0 = 32 * nb + 8 * a + 4 * g;
       E::store4(orow + d0 * E::kElem, eng.o[nb][4 * a] * inv, eng.o[nb][4 * a + 1] * inv,
                 eng.o[nb][4 * a + 2] * inv, eng.o[nb][4 * a + 3] * inv);
     }
-  if (p.lse && g == 0) p.lse[(size_t)bh * p.N + row] = (M + __log2f(Lt)) * 0.69314718055994531f;
+  if (p.lse && g == 0) p.lse[(size_t)bh * p.N + row] = (sm.M + __log2f(Lt)) * 0.69314718055994531f;
 }
 
 // Exact merge of the text-row partials: M = max_s M_s, w_s = 2^(M_s - M),
@@ -526,16 +591,15 @@ __global__ void __launch_bounds__(D) clear_text_merge_kernel(Params p) {
     M = fmaxf(M, p.ws_ml[(((size_t)s * p.BH + bh) * p.n_text + tq) * 2]);
   float L = 0.0f, acc = 0.0f;
   for (int s = 0; s < p.splits; ++s) {
-    size_t base = ((size_t)s * p.BH + bh) * p.n_text + tq;
-    float w = __builtin_amdgcn_exp2f(p.ws_ml[base * 2] - M);
+    const size_t base = ((size_t)s * p.BH + bh) * p.n_text + tq;
+    const float w = __builtin_amdgcn_exp2f(p.ws_ml[base * 2] - M);
     L += w * p.ws_ml[base * 2 + 1];
     acc += w * p.ws_o[base * D + d];
   }
-  float o = L > 0.0f ? acc / L : 0.0f;
-  size_t oi = ((size_t)bh * p.N + tq) * D + d;
+  const float o = L > 0.0f ? acc / L : 0.0f;
+  const size_t oi = ((size_t)bh * p.N + tq) * D + d;
   if constexpr (BF16) {
-    __bf16 h = (__bf16)o;
-    ((__bf16*)p.out)[oi] = h;
+    ((__bf16*)p.out)[oi] = (__bf16)o;
   } else {
     ((float*)p.out)[oi] = o;
   }
@@ -603,7 +667,7 @@ int attn_launch(const AttnLaunch& a, void* stream) {
       if (a.d == 128) hipLaunchKernelGGL((clear_text_merge_kernel<128, false>), dim3(rows), dim3(128), 0, s, p);
       else hipLaunchKernelGGL((clear_text_merge_kernel<64, false>), dim3(rows), dim3(64), 0, s, p);
     }
-    hipError_t e = hipGetLastError();
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return set_error(CLEAR_EHIP, "merge kernel launch: %s", hipGetErrorString(e));
   }
   return CLEAR_OK;

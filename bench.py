@@ -62,7 +62,7 @@ def computed_pairs(ca, n_text: int, gh: int, gw: int, r2: int) -> int:
 
     tm = ca.tile_map_build(gh, gw, r2)
     f = tm["flags"].astype(np.int64)
-    per_wave_img = sum(int(((f >> w) & 1).sum()) for w in range(4)) * ca.CHUNK * 32
+    per_wave_img = sum(int(((f >> w) & 1).sum()) for w in range(4)) * ca.KEY_H * ca.KEY_W * 32
     ntx = -(-gw // ca.TILE_W)
     nty = -(-gh // ca.TILE_H)
     waves_on = sum(min(4, max(0, -(-(gh - ty * 16) // 4))) for ty in range(nty)) * ntx
@@ -178,6 +178,9 @@ def main():
     ap.add_argument("--also-radius", type=int, default=8, help="second radius timed alongside (-1: none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (3 times) and exit: "
+                         "the reference for scaling the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -191,8 +194,17 @@ def main():
     import dit_circular_local_amd as ca
     from dit_circular_local_amd.inputs import WORKLOADS, workload_qkv
 
-    w = WORKLOADS[args.workload]
     torch.cuda.set_device(0)
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_probe_mib} MiB x3")
+        return
+    w = WORKLOADS[args.workload]
     log(f"generating {w.name} inputs (seeded)...")
     t0 = time.perf_counter()
     q, k, v = workload_qkv(w, seed=0, device="cuda")

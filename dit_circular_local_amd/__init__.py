@@ -21,14 +21,15 @@ __all__ = [
     "ClearError", "fwd", "tile_map_size", "tile_map_build", "tile_map_build_device",
     "release_cache", "last_error", "version", "lib", "EXPORTS",
     "CLEAR_OK", "CLEAR_EINVAL", "CLEAR_ENOMEM", "CLEAR_EHIP", "CLEAR_ENOTSUP",
-    "CLEAR_BF16", "CLEAR_FP32", "TILE_H", "TILE_W", "SUB_H", "SUB_W", "CHUNK", "MAX_GRID",
+    "CLEAR_BF16", "CLEAR_FP32", "TILE_H", "TILE_W", "SUB_H", "SUB_W", "KEY_H", "KEY_W", "CHUNK",
+    "MAX_GRID",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libclear_attn.so")
 
 CLEAR_OK, CLEAR_EINVAL, CLEAR_ENOMEM, CLEAR_EHIP, CLEAR_ENOTSUP = 0, -22, -12, -5, -95
 CLEAR_BF16, CLEAR_FP32 = 0, 1
-TILE_H, TILE_W, SUB_H, SUB_W, CHUNK = 16, 8, 4, 8, 32
+TILE_H, TILE_W, SUB_H, SUB_W, KEY_H, KEY_W, CHUNK = 16, 8, 4, 8, 4, 8, 32
 MAX_GRID = 8192
 
 # every entry point declared in include/clear_attn.h
@@ -66,11 +67,11 @@ def lib():
     L.clear_attn_fwd.restype = i
     L.clear_attn_fwd_ex.argtypes = [p, p, p, p, i, i, i, i, i, i, ctypes.POINTER(_Opts), p]
     L.clear_attn_fwd_ex.restype = i
-    L.clear_tile_map_size.argtypes = [i, i, i, i, i, i, i, i, szp, szp]
+    L.clear_tile_map_size.argtypes = [i, i, i, i, i, i, i, i, i, szp]
     L.clear_tile_map_size.restype = i
-    L.clear_tile_map_build.argtypes = [i, i, i, i, i, i, i, i, p, p, sz, p, p, sz, szp, szp]
+    L.clear_tile_map_build.argtypes = [i, i, i, i, i, i, i, i, i, p, p, p, sz, szp]
     L.clear_tile_map_build.restype = i
-    L.clear_tile_map_build_device.argtypes = [i, i, i, i, i, i, i, i, p, p, sz, p, p, sz, szp, szp, p]
+    L.clear_tile_map_build_device.argtypes = [i, i, i, i, i, i, i, i, i, p, p, p, sz, szp, p]
     L.clear_tile_map_build_device.restype = i
     L.clear_last_error.argtypes = []
     L.clear_last_error.restype = ctypes.c_char_p
@@ -159,11 +160,11 @@ def fwd(q, k, v, n_text: int, grid_h: int, grid_w: int, radius: Optional[int] = 
 
 
 def tile_map_size(grid_h, grid_w, r2, tile_h=TILE_H, tile_w=TILE_W, sub_h=SUB_H, sub_w=SUB_W,
-                  chunk=CHUNK):
-    nr, nc = ctypes.c_size_t(), ctypes.c_size_t()
-    _check(lib().clear_tile_map_size(grid_h, grid_w, r2, tile_h, tile_w, sub_h, sub_w, chunk,
-                                     ctypes.byref(nr), ctypes.byref(nc)))
-    return nr.value, nc.value
+                  key_h=KEY_H, key_w=KEY_W):
+    n = ctypes.c_size_t()
+    _check(lib().clear_tile_map_size(grid_h, grid_w, r2, tile_h, tile_w, sub_h, sub_w, key_h, key_w,
+                                     ctypes.byref(n)))
+    return n.value
 
 
 def _ntiles(grid_h, grid_w, tile_h, tile_w):
@@ -171,43 +172,39 @@ def _ntiles(grid_h, grid_w, tile_h, tile_w):
 
 
 def tile_map_build(grid_h, grid_w, r2, tile_h=TILE_H, tile_w=TILE_W, sub_h=SUB_H, sub_w=SUB_W,
-                   chunk=CHUNK):
+                   key_h=KEY_H, key_w=KEY_W):
     """Host-built tile map as numpy arrays (layout in include/clear_attn.h)."""
     L = lib()
-    nr, nc = tile_map_size(grid_h, grid_w, r2, tile_h, tile_w, sub_h, sub_w, chunk)
+    n = tile_map_size(grid_h, grid_w, r2, tile_h, tile_w, sub_h, sub_w, key_h, key_w)
     nt = _ntiles(grid_h, grid_w, tile_h, tile_w)
-    ro = np.zeros(nt + 1, np.uint32)
-    runs = np.zeros((max(nr, 1), 2), np.uint32)
-    co = np.zeros(nt + 1, np.uint32)
-    fl = np.zeros(max(nc, 1), np.uint16)
-    a, b = ctypes.c_size_t(), ctypes.c_size_t()
-    _check(L.clear_tile_map_build(grid_h, grid_w, r2, tile_h, tile_w, sub_h, sub_w, chunk,
-                                  ro.ctypes.data, runs.ctypes.data, nr, co.ctypes.data,
-                                  fl.ctypes.data, nc, ctypes.byref(a), ctypes.byref(b)))
-    return {"run_offsets": ro, "runs": runs[:nr], "chunk_offsets": co, "flags": fl[:nc]}
+    off = np.zeros(nt + 1, np.uint32)
+    kt = np.zeros(max(n, 1), np.uint32)
+    fl = np.zeros(max(n, 1), np.uint16)
+    got = ctypes.c_size_t()
+    _check(L.clear_tile_map_build(grid_h, grid_w, r2, tile_h, tile_w, sub_h, sub_w, key_h, key_w,
+                                  off.ctypes.data, kt.ctypes.data, fl.ctypes.data, n,
+                                  ctypes.byref(got)))
+    return {"offsets": off, "key_tiles": kt[:n], "flags": fl[:n]}
 
 
 def tile_map_build_device(grid_h, grid_w, r2, tile_h=TILE_H, tile_w=TILE_W, sub_h=SUB_H,
-                          sub_w=SUB_W, chunk=CHUNK, device="cuda"):
+                          sub_w=SUB_W, key_h=KEY_H, key_w=KEY_W, device="cuda"):
     """Device-built tile map; returns numpy copies of the device arrays."""
     import torch
 
     L = lib()
-    nr, nc = tile_map_size(grid_h, grid_w, r2, tile_h, tile_w, sub_h, sub_w, chunk)
+    n = tile_map_size(grid_h, grid_w, r2, tile_h, tile_w, sub_h, sub_w, key_h, key_w)
     nt = _ntiles(grid_h, grid_w, tile_h, tile_w)
-    ro = torch.zeros(nt + 1, dtype=torch.int32, device=device)
-    runs = torch.zeros(max(nr, 1) * 2, dtype=torch.int32, device=device)
-    co = torch.zeros(nt + 1, dtype=torch.int32, device=device)
-    fl = torch.zeros(max(nc, 1), dtype=torch.int16, device=device)
-    a, b = ctypes.c_size_t(), ctypes.c_size_t()
-    _check(L.clear_tile_map_build_device(grid_h, grid_w, r2, tile_h, tile_w, sub_h, sub_w, chunk,
-                                         ro.data_ptr(), runs.data_ptr(), nr, co.data_ptr(),
-                                         fl.data_ptr(), nc, ctypes.byref(a), ctypes.byref(b),
-                                         _stream_of(ro)))
-    torch.cuda.current_stream(ro.device).synchronize()
+    off = torch.zeros(nt + 1, dtype=torch.int32, device=device)
+    kt = torch.zeros(max(n, 1), dtype=torch.int32, device=device)
+    fl = torch.zeros(max(n, 1), dtype=torch.int16, device=device)
+    got = ctypes.c_size_t()
+    _check(L.clear_tile_map_build_device(grid_h, grid_w, r2, tile_h, tile_w, sub_h, sub_w, key_h,
+                                         key_w, off.data_ptr(), kt.data_ptr(), fl.data_ptr(), n,
+                                         ctypes.byref(got), _stream_of(off)))
+    torch.cuda.current_stream(off.device).synchronize()
     return {
-        "run_offsets": ro.cpu().numpy().view(np.uint32),
-        "runs": runs.cpu().numpy().view(np.uint32).reshape(-1, 2)[:nr],
-        "chunk_offsets": co.cpu().numpy().view(np.uint32),
-        "flags": fl.cpu().numpy().view(np.uint16)[:nc],
+        "offsets": off.cpu().numpy().view(np.uint32),
+        "key_tiles": kt.cpu().numpy().view(np.uint32)[:n],
+        "flags": fl.cpu().numpy().view(np.uint16)[:n],
     }

@@ -9,10 +9,10 @@
 // Work decomposition (one launch):
 //  * image workgroups: 256 threads = 4 wavefronts own a 16 x 8 cell query tile,
 //    each wavefront a 4 x 8 sub-tile (32 queries).  Keys stream through LDS in
-//    chunks of 32: first the text keys, then the tile's key list (one run of
-//    columns per key row, from the tile map).  A wavefront skips chunks its
-//    sub-tile does not touch and applies the per-element circular mask only on
-//    chunks it does not fully admit;
+//    chunks of 32: first the text keys, then the 4 x 8 cell key tiles the tile
+//    map lists for the query tile.  A wavefront skips key tiles its sub-tile does
+//    not touch and applies the per-element circular mask only to key tiles it
+//    does not fully admit;
 //  * text workgroups: 128 text queries against a contiguous range of all keys
 //    (the range is one of `splits` parts; partial results are merged exactly by
 //    log-sum-exp in a second kernel when splits > 1).
@@ -60,15 +60,17 @@ constexpr int kTileW = CLEAR_TILE_W;
 constexpr int kSubH = CLEAR_SUB_H;
 constexpr int kChunk = CLEAR_CHUNK;
 constexpr int kStages = 3;
-constexpr int kMaxLdsRuns = 256;     // tiles with more key rows fall back to global run reads
+constexpr int kKeyH = CLEAR_KEY_H;
+constexpr int kKeyW = CLEAR_KEY_W;
 constexpr int kTextQ = kWaves * 32;  // text queries per workgroup
 constexpr float kLazyTau = 8.0f;
 constexpr float kMInit = -1.0e30f;
-constexpr short kCoordFar = -16384;  // key y of padding positions: never admitted
 
 static_assert(kTileH == kWaves * kSubH && kTileW == CLEAR_SUB_W && kTileW * kSubH == 32,
               "one 32-query sub-tile per wavefront");
 static_assert(kChunk == 32, "chunk = one 32-row MFMA block");
+static_assert(kKeyH * kKeyW == kChunk && kKeyW == 8,
+              "key tile = one chunk; key cell (a, c) is chunk position 8a + c");
 
 struct Params {
   const char* q;
@@ -78,12 +80,11 @@ struct Params {
   float* lse;
   float* ws_o;
   float* ws_ml;
-  const uint32_t* run_off;
-  const uint32_t* runs;
-  const uint32_t* chunk_off;
-  const uint16_t* flags;
+  const uint32_t* tm_offsets;
+  const uint32_t* tm_key_tiles;
+  const uint16_t* tm_flags;
   int N, n_text, gh, gw, r2;
-  int ntiles, ntx;
+  int ntiles, ntx, nkx;
   int n_text_blocks, splits, chunks_per_split;
   int n_text_wg, n_text_wg_pad, n_img_wg, BH;
   float scale_log2;
@@ -116,12 +117,12 @@ struct Bf16 {
   static constexpr int kRowV = D * 2 + 64;
   static constexpr int kKOff = 0;
   static constexpr int kVOff = kChunk * kRowK;
-  static constexpr int kCOff = kVOff + kChunk * kRowV;
-  static constexpr int kFOff = kCOff + kChunk * 4;
-  static constexpr int kStage = kFOff + 16;
+  static constexpr int kMOff = kVOff + kChunk * kRowV;   // chunk meta: flags, ky0, kx0
+  static constexpr int kStage = kMOff + 16;
   static constexpr int kKIters = kChunk * kPPR / kThreads;
   static constexpr int kKK = D / 16;
   static constexpr int kNB = D / 32;
+  static constexpr int kWavesPerSimd = 2;   // two workgroups per CU
   static_assert(kChunk * kPPR % kThreads == 0, "pieces must split evenly");
 
   bf16x8_t q[kKK];
@@ -195,12 +196,12 @@ struct F32 {
   static constexpr int kRowV = D * 4 + 16;
   static constexpr int kKOff = 0;
   static constexpr int kVOff = kChunk * kRowK;
-  static constexpr int kCOff = kVOff + kChunk * kRowV;
-  static constexpr int kFOff = kCOff + kChunk * 4;
-  static constexpr int kStage = kFOff + 16;
+  static constexpr int kMOff = kVOff + kChunk * kRowV;   // chunk meta: flags, ky0, kx0
+  static constexpr int kStage = kMOff + 16;
   static constexpr int kKIters = kChunk * kPPR / kThreads;
   static constexpr int kHalf = D / 2;   // d values per lane group in Q.K
   static constexpr int kNB = D / 32;
+  static constexpr int kWavesPerSimd = 1;
   static_assert(kChunk * kPPR % kThreads == 0, "pieces must split evenly");
 
   float q[kHalf];
@@ -241,95 +242,60 @@ struct F32 {
 
 // Maps (chunk j, position p) to a key token for the current workgroup.
 // Chunks 0 .. n_dense-1 are a dense token range (the text keys of an image
-// tile, or a key range of a text workgroup); the rest walk the tile's runs.
+// tile, or a key range of a text workgroup); chunk n_dense + e is the e-th key
+// tile the tile map lists for the query tile, position p = 8a + c being its
+// key cell (ky0 + a, kx0 + c).
 struct KeySource {
   int dense_base, dense_limit, n_dense;
-  int n_text, gw;
-  uint32_t total;          // keys in the tile's list
-  int nr;                  // runs of the tile
-  bool lds;                // runs cached in LDS (flat offsets and packed start cells)
-  const uint32_t* g_runs;  // the tile's runs in global memory (start, length)
-  const uint32_t* l_off;   // LDS [nr + 1] flat offset of each run
-  const uint32_t* l_pos;   // LDS [nr] (ky << 16) | kx of each run's first key
-  int cur;                 // run containing the first position of the current chunk
-  uint32_t cur_base;       // its flat offset (global path)
-
-  // Move the cursor to flat position f0 (non-decreasing across calls).
-  __device__ void seek(uint32_t f0) {
-    if (lds) {
-      while (cur + 1 < nr && l_off[cur + 1] <= f0) ++cur;
-    } else {
-      while (cur + 1 < nr && cur_base + g_runs[2 * cur + 1] <= f0) {
-        cur_base += g_runs[2 * cur + 1];
-        ++cur;
-      }
-    }
-  }
-  // Token of position p of chunk j; out-of-range positions return a clamped,
-  // in-bounds token with valid = false.  (ky, kx) are the key's grid cell.
-  __device__ int token(int j, int p, bool& valid, int& ky, int& kx) const {
-    if (j < n_dense) {
-      int t = dense_base + j * kChunk + p;
-      valid = t < dense_limit;
-      ky = 0;
-      kx = 0;
-      return valid ? t : dense_limit - 1;
-    }
-    uint32_t f = (uint32_t)(j - n_dense) * kChunk + p;
-    valid = f < total;
-    if (!valid) f = total - 1;
-    if (lds) {
-      int i = cur;
-      while (i + 1 < nr && l_off[i + 1] <= f) ++i;
-      const uint32_t pos = l_pos[i];
-      ky = (int)(pos >> 16);
-      kx = (int)(pos & 0xffffu) + (int)(f - l_off[i]);
-    } else {
-      int i = cur;
-      uint32_t b = cur_base;
-      while (i + 1 < nr && f >= b + g_runs[2 * i + 1]) {
-        b += g_runs[2 * i + 1];
-        ++i;
-      }
-      const uint32_t s = g_runs[2 * i];
-      ky = (int)(s / (uint32_t)gw);
-      kx = (int)(s - (uint32_t)ky * (uint32_t)gw) + (int)(f - b);
-    }
-    return n_text + ky * gw + kx;
-  }
+  int n_text, gh, gw, nkx;
+  const uint32_t* key_tiles;  // the query tile's entries
+  const uint16_t* flags;
 };
 
-// One chunk in flight in registers: K and V pieces, packed key cells, chunk flags.
+// One chunk in flight in registers: K and V pieces of this thread, and the
+// chunk's flags and key-tile origin (uniform).
 template <class E>
 struct RegSet {
   u32x4_t k[E::kKIters];
   u32x4_t v[E::kKIters];
-  unsigned c[E::kKIters];
   unsigned flag;
+  int ky0, kx0;
 };
 
 __device__ __forceinline__ int kpos_of(int r, int ppr) { return (threadIdx.x + r * kThreads) / ppr; }
 __device__ __forceinline__ int kcol_of(int r, int ppr) { return (threadIdx.x + r * kThreads) % ppr; }
 
 template <class E>
-__device__ __forceinline__ void gather(RegSet<E>& rs, KeySource& ks, int j, const char* kbase,
-                                       const char* vbase, const uint16_t* flags, int co) {
-  if (j >= ks.n_dense) {
-    ks.seek((uint32_t)(j - ks.n_dense) * kChunk);
-    rs.flag = flags[co + (j - ks.n_dense)];
-  } else {
+__device__ __forceinline__ void gather(RegSet<E>& rs, const KeySource& ks, int j, const char* kbase,
+                                       const char* vbase) {
+  int tok[E::kKIters];
+  if (j < ks.n_dense) {
     rs.flag = 0;
+    rs.ky0 = 0;
+    rs.kx0 = 0;
+    for (int r = 0; r < E::kKIters; ++r) {
+      const int t = ks.dense_base + j * kChunk + kpos_of(r, E::kPPR);
+      tok[r] = t < ks.dense_limit ? t : ks.dense_limit - 1;
+    }
+  } else {
+    const int e = j - ks.n_dense;
+    const int kt = (int)ks.key_tiles[e];
+    rs.flag = ks.flags[e];
+    const int kty = kt / ks.nkx;
+    rs.ky0 = kty * kKeyH;
+    rs.kx0 = (kt - kty * ks.nkx) * kKeyW;
+    for (int r = 0; r < E::kKIters; ++r) {
+      const int p = kpos_of(r, E::kPPR);
+      // cells past the grid edge load an in-grid row; the mask drops them
+      const int ky = min(rs.ky0 + (p >> 3), ks.gh - 1);
+      const int kx = min(rs.kx0 + (p & 7), ks.gw - 1);
+      tok[r] = ks.n_text + ky * ks.gw + kx;
+    }
   }
   for (int r = 0; r < E::kKIters; ++r) {
-    bool valid;
-    int ky, kx;
-    const int tok = ks.token(j, kpos_of(r, E::kPPR), valid, ky, kx);
-    const size_t off = (size_t)tok * E::kRowBytes + kcol_of(r, E::kPPR) * 16;
+    const size_t off = (size_t)tok[r] * E::kRowBytes + kcol_of(r, E::kPPR) * 16;
     rs.k[r] = *(const u32x4_t*)(kbase + off);
     rs.v[r] = *(const u32x4_t*)(vbase + off);
-    const short cy = valid ? (short)ky : kCoordFar;
-    const short cx = valid ? (short)kx : (short)0;
-    rs.c[r] = (unsigned)(unsigned short)cx | ((unsigned)(unsigned short)cy << 16);
   }
 }
 
@@ -339,9 +305,13 @@ __device__ __forceinline__ void lstore(char* st, const RegSet<E>& rs) {
     const int pos = kpos_of(r, E::kPPR), col = kcol_of(r, E::kPPR);
     *(u32x4_t*)(st + E::kKOff + pos * E::kRowK + col * 16) = rs.k[r];
     *(u32x4_t*)(st + E::kVOff + pos * E::kRowV + col * 16) = rs.v[r];
-    if (col == 0) *(unsigned*)(st + E::kCOff + pos * 4) = rs.c[r];
   }
-  if (threadIdx.x == 0) *(unsigned*)(st + E::kFOff) = rs.flag;
+  if (threadIdx.x == 0) {
+    int* m = (int*)(st + E::kMOff);
+    m[0] = (int)rs.flag;
+    m[1] = rs.ky0;
+    m[2] = rs.kx0;
+  }
 }
 
 struct SoftmaxState {
@@ -351,18 +321,22 @@ struct SoftmaxState {
 // Consume one chunk from LDS stage `st` (one wavefront).
 template <class E>
 __device__ __forceinline__ void compute_chunk(E& eng, SoftmaxState& sm, const char* st, int j,
-                                              const KeySource& ks, int lane, int wave,
-                                              s16x2_t qc, int r2, float scale_log2) {
+                                              const KeySource& ks, int lane, int wave, int qy,
+                                              int qx, int r2, float scale_log2) {
   const int g = lane >> 5;
   int tail = 32;  // dense chunk: positions >= tail are masked
   bool coord_mask = false;
+  int ky0 = 0, kx0 = 0;
   if (j < ks.n_dense) {
     const int rem_keys = ks.dense_limit - (ks.dense_base + j * kChunk);
     tail = rem_keys < 32 ? rem_keys : 32;
   } else {
-    const unsigned f = *(const unsigned*)(st + E::kFOff);
+    const int* m = (const int*)(st + E::kMOff);
+    const unsigned f = (unsigned)m[0];
     if (!((f >> wave) & 1u)) return;
     coord_mask = !((f >> (8 + wave)) & 1u);
+    ky0 = m[1];
+    kx0 = m[2];
   }
 
   f32x16_t s;
@@ -372,19 +346,20 @@ __device__ __forceinline__ void compute_chunk(E& eng, SoftmaxState& sm, const ch
     for (int i = 0; i < 16; ++i)
       if (acc_row(i, g) >= tail) s[i] = -__builtin_inff();
   } else if (coord_mask) {
-    const u32x4_t* cp = (const u32x4_t*)(st + E::kCOff);
+    // Register i of lane group g holds key cell (ky0 + i/4, kx0 + 4g + i%4) of
+    // the key tile; admitted iff dx^2 <= r2 - dy^2 with both cells on the grid.
+    int lim[4], dxx[4];
     for (int a = 0; a < 4; ++a) {
-      const u32x4_t c4 = cp[2 * a + g];  // positions 8a + 4g .. 8a + 4g + 3
-      for (int b = 0; b < 4; ++b) {
-        // (built from shifts: a bit_cast of the vector element itself was
-        // compiled as element 0 for every b)
-        const unsigned cv = c4[b];
-        const s16x2_t kc = {(short)(cv & 0xffffu), (short)(cv >> 16)};
-        const s16x2_t dd = qc - kc;
-        const int d2 = __builtin_amdgcn_sdot2(dd, dd, 0, false);
-        if (d2 > r2) s[4 * a + b] = -__builtin_inff();
-      }
+      const int dy = qy - ky0 - a;
+      lim[a] = ky0 + a < ks.gh ? r2 - dy * dy : -1;
     }
+    for (int b = 0; b < 4; ++b) {
+      const int kx = kx0 + 4 * g + b;
+      const int dx = qx - kx;
+      dxx[b] = kx < ks.gw ? dx * dx : 0x7fffffff;
+    }
+    for (int i = 0; i < 16; ++i)
+      if (dxx[i & 3] > lim[i >> 2]) s[i] = -__builtin_inff();
   }
 
   // online softmax (base 2, lazy reference max)
@@ -411,10 +386,8 @@ __device__ __forceinline__ void compute_chunk(E& eng, SoftmaxState& sm, const ch
 }
 
 template <class E>
-__global__ void __launch_bounds__(kThreads, 2) clear_attn_fwd_kernel(Params p) {
+__global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char smem[kStages * E::kStage];
-  __shared__ uint32_t l_off[kMaxLdsRuns + 1];
-  __shared__ uint32_t l_pos[kMaxLdsRuns];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -429,18 +402,13 @@ __global__ void __launch_bounds__(kThreads, 2) clear_attn_fwd_kernel(Params p) {
   bool qvalid;
   KeySource ks;
   ks.n_text = p.n_text;
+  ks.gh = p.gh;
   ks.gw = p.gw;
-  ks.total = 0;
-  ks.nr = 0;
-  ks.lds = true;
-  ks.g_runs = p.runs;
-  ks.l_off = l_off;
-  ks.l_pos = l_pos;
-  ks.cur = 0;
-  ks.cur_base = 0;
+  ks.nkx = p.nkx;
+  ks.key_tiles = p.tm_key_tiles;
+  ks.flags = p.tm_flags;
   int n_chunks;
   int split = 0, tq = 0;
-  int co = 0;
   if (text_wg) {
     split = bid % p.splits;
     const int rest = bid / p.splits;
@@ -474,37 +442,10 @@ __global__ void __launch_bounds__(kThreads, 2) clear_attn_fwd_kernel(Params p) {
     ks.dense_base = 0;
     ks.dense_limit = p.n_text;
     ks.n_dense = (p.n_text + kChunk - 1) / kChunk;
-    const int r_begin = (int)p.run_off[tile];
-    const int nr = (int)p.run_off[tile + 1] - r_begin;
-    ks.nr = nr;
-    ks.g_runs = p.runs + 2 * (size_t)r_begin;
-    ks.lds = nr <= kMaxLdsRuns;
-    if (ks.lds) {
-      // runs -> LDS: packed first cell and an exclusive scan of the lengths
-      uint32_t len = 0;
-      if (tid < nr) {
-        const uint32_t s = ks.g_runs[2 * tid];
-        len = ks.g_runs[2 * tid + 1];
-        const uint32_t y = s / (uint32_t)p.gw;
-        l_pos[tid] = (y << 16) | (s - y * (uint32_t)p.gw);
-      }
-      l_off[tid + 1] = len;
-      if (tid == 0) l_off[0] = 0;
-      __syncthreads();
-      for (int d = 1; d < kMaxLdsRuns; d <<= 1) {
-        const uint32_t x = tid + 1 > d ? l_off[tid + 1 - d] : 0u;
-        __syncthreads();
-        l_off[tid + 1] += x;
-        __syncthreads();
-      }
-      ks.total = nr > 0 ? l_off[nr] : 0u;
-    } else {
-      uint32_t tot = 0;
-      for (int i = 0; i < nr; ++i) tot += ks.g_runs[2 * i + 1];
-      ks.total = tot;
-    }
-    co = (int)p.chunk_off[tile];
-    n_chunks = ks.n_dense + (int)(p.chunk_off[tile + 1] - p.chunk_off[tile]);
+    const uint32_t e0 = p.tm_offsets[tile];
+    ks.key_tiles = p.tm_key_tiles + e0;
+    ks.flags = p.tm_flags + e0;
+    n_chunks = ks.n_dense + (int)(p.tm_offsets[tile + 1] - e0);
   }
 
   const size_t head_off = (size_t)bh * p.N * E::kRowBytes;
@@ -515,34 +456,34 @@ __global__ void __launch_bounds__(kThreads, 2) clear_attn_fwd_kernel(Params p) {
   eng.load_q(p.q + head_off + (size_t)(qvalid ? qtok : 0) * E::kRowBytes, qvalid, g);
   eng.zero_o();
   const bool wave_active = __ballot(qvalid) != 0ull;
-  const s16x2_t qc = {(short)qx, (short)qy};
   SoftmaxState sm{kMInit, 0.0f};
 
   // ---- pipelined main loop: chunk c in register set c % 2, LDS stage c % 3
   RegSet<E> s0, s1;
   const int n = n_chunks;
-  if (n > 0) gather(s0, ks, 0, kbase, vbase, p.flags, co);
-  if (n > 1) gather(s1, ks, 1, kbase, vbase, p.flags, co);
+  if (n > 0) gather(s0, ks, 0, kbase, vbase);
+  if (n > 1) gather(s1, ks, 1, kbase, vbase);
   if (n > 0) lstore(smem, s0);
-  if (n > 2) gather(s0, ks, 2, kbase, vbase, p.flags, co);
+  if (n > 2) gather(s0, ks, 2, kbase, vbase);
   int st_cur = 0;  // stage of chunk j
   for (int j = 0; j < n; j += 2) {
     {
       const int st_next = st_cur == kStages - 1 ? 0 : st_cur + 1;
       if (j + 1 < n) lstore(smem + st_next * E::kStage, s1);
-      if (j + 3 < n) gather(s1, ks, j + 3, kbase, vbase, p.flags, co);
+      if (j + 3 < n) gather(s1, ks, j + 3, kbase, vbase);
       __syncthreads();
       if (wave_active)
-        compute_chunk(eng, sm, smem + st_cur * E::kStage, j, ks, lane, wave, qc, p.r2, p.scale_log2);
+        compute_chunk(eng, sm, smem + st_cur * E::kStage, j, ks, lane, wave, qy, qx, p.r2,
+                      p.scale_log2);
       st_cur = st_next;
     }
     if (j + 1 < n) {
       const int st_next = st_cur == kStages - 1 ? 0 : st_cur + 1;
       if (j + 2 < n) lstore(smem + st_next * E::kStage, s0);
-      if (j + 4 < n) gather(s0, ks, j + 4, kbase, vbase, p.flags, co);
+      if (j + 4 < n) gather(s0, ks, j + 4, kbase, vbase);
       __syncthreads();
       if (wave_active)
-        compute_chunk(eng, sm, smem + st_cur * E::kStage, j + 1, ks, lane, wave, qc, p.r2,
+        compute_chunk(eng, sm, smem + st_cur * E::kStage, j + 1, ks, lane, wave, qy, qx, p.r2,
                       p.scale_log2);
       st_cur = st_next;
     }
@@ -624,10 +565,9 @@ int attn_launch(const AttnLaunch& a, void* stream) {
   p.lse = a.lse;
   p.ws_o = a.ws_o;
   p.ws_ml = a.ws_ml;
-  p.run_off = a.run_off;
-  p.runs = a.runs;
-  p.chunk_off = a.chunk_off;
-  p.flags = a.flags;
+  p.tm_offsets = a.tm_offsets;
+  p.tm_key_tiles = a.tm_key_tiles;
+  p.tm_flags = a.tm_flags;
   p.N = a.n_text + a.gh * a.gw;
   p.n_text = a.n_text;
   p.gh = a.gh;
@@ -635,6 +575,7 @@ int attn_launch(const AttnLaunch& a, void* stream) {
   p.r2 = a.r2;
   p.ntx = (a.gw + kTileW - 1) / kTileW;
   p.ntiles = ((a.gh + kTileH - 1) / kTileH) * p.ntx;
+  p.nkx = (a.gw + kKeyW - 1) / kKeyW;
   p.BH = a.B * a.H;
   p.n_text_blocks = (a.n_text + kTextQ - 1) / kTextQ;
   const int nall = (p.N + kChunk - 1) / kChunk;

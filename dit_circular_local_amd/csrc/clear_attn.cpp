@@ -18,12 +18,11 @@ namespace {
 thread_local char g_err[512];
 
 struct TileMapDev {
-  void* block = nullptr;  // one allocation holding the four arrays
-  uint32_t* run_off = nullptr;
-  uint32_t* runs = nullptr;
-  uint32_t* chunk_off = nullptr;
+  void* block = nullptr;  // one allocation holding the three arrays
+  uint32_t* offsets = nullptr;
+  uint32_t* key_tiles = nullptr;
   uint16_t* flags = nullptr;
-  size_t n_runs = 0, n_chunks = 0;
+  size_t n_entries = 0;
   hipEvent_t ready = nullptr;  // recorded after the build kernels
 };
 
@@ -45,7 +44,8 @@ int hip_fail(hipError_t e, const char* what) {
 // Tile map of the kernels' fixed tiling for (gh, gw, r2) on the current device;
 // built on `stream` on first use.  Caller holds g_mu.
 int get_tile_map(DevState& ds, int gh, int gw, int r2, hipStream_t stream, TileMapDev** out) {
-  TileGeom g = make_geom(gh, gw, r2, CLEAR_TILE_H, CLEAR_TILE_W, CLEAR_SUB_H, CLEAR_SUB_W, CLEAR_CHUNK);
+  TileGeom g = make_geom(gh, gw, r2, CLEAR_TILE_H, CLEAR_TILE_W, CLEAR_SUB_H, CLEAR_SUB_W, CLEAR_KEY_H,
+                         CLEAR_KEY_W);
   auto key = std::make_tuple(gh, gw, g.r2);
   auto it = ds.maps.find(key);
   if (it != ds.maps.end()) {
@@ -53,21 +53,18 @@ int get_tile_map(DevState& ds, int gh, int gw, int r2, hipStream_t stream, TileM
     return CLEAR_OK;
   }
   TileMapDev m;
-  tile_map_counts(g, &m.n_runs, &m.n_chunks, nullptr, nullptr);
+  m.n_entries = tile_map_count(g);
   const size_t nt = (size_t)g.nty * g.ntx;
-  const size_t o_ro = 0;
-  const size_t o_runs = align_up(o_ro + (nt + 1) * 4, 256);
-  const size_t o_co = align_up(o_runs + m.n_runs * 8, 256);
-  const size_t o_fl = align_up(o_co + (nt + 1) * 4, 256);
-  const size_t bytes = align_up(o_fl + m.n_chunks * 2 + 2, 256);
+  const size_t o_kt = align_up((nt + 1) * 4, 256);
+  const size_t o_fl = align_up(o_kt + m.n_entries * 4, 256);
+  const size_t bytes = align_up(o_fl + m.n_entries * 2 + 2, 256);
   hipError_t e = hipMalloc(&m.block, bytes);
   if (e != hipSuccess) return set_error(CLEAR_ENOMEM, "tile map allocation (%zu bytes): %s", bytes, hipGetErrorString(e));
   char* b = (char*)m.block;
-  m.run_off = (uint32_t*)(b + o_ro);
-  m.runs = (uint32_t*)(b + o_runs);
-  m.chunk_off = (uint32_t*)(b + o_co);
+  m.offsets = (uint32_t*)b;
+  m.key_tiles = (uint32_t*)(b + o_kt);
   m.flags = (uint16_t*)(b + o_fl);
-  int rc = tile_map_build_device_launch(g, m.run_off, m.runs, m.chunk_off, m.flags, nullptr, stream);
+  int rc = tile_map_build_device_launch(g, m.offsets, m.key_tiles, m.flags, stream);
   if (rc) {
     (void)hipFree(m.block);
     return rc;
@@ -86,6 +83,7 @@ int get_tile_map(DevState& ds, int gh, int gw, int r2, hipStream_t stream, TileM
 // Text-row split count: make a text workgroup's key range (its critical path)
 // at most about half of the ideal time of the whole launch.
 int choose_text_splits(int B, int H, int n_text, int N, int ntiles, size_t img_chunks) {
+  // img_chunks: listed key tiles (32 keys each) over all query tiles
   if (n_text == 0) return 1;
   const double nall = (N + CLEAR_CHUNK - 1) / CLEAR_CHUNK;
   const double text_blocks = (n_text + 127) / 128;
@@ -178,13 +176,14 @@ extern "C" int clear_attn_fwd_ex(const void* q, const void* k, const void* v, vo
   if (rc) return rc;
   if ((e = hipStreamWaitEvent(s, tm->ready, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
 
-  TileGeom g = make_geom(grid_h, grid_w, o.r2_max, CLEAR_TILE_H, CLEAR_TILE_W, CLEAR_SUB_H, CLEAR_SUB_W, CLEAR_CHUNK);
+  TileGeom g = make_geom(grid_h, grid_w, o.r2_max, CLEAR_TILE_H, CLEAR_TILE_W, CLEAR_SUB_H, CLEAR_SUB_W,
+                         CLEAR_KEY_H, CLEAR_KEY_W);
   int splits = o.text_splits ? o.text_splits
-                             : choose_text_splits(B, H, n_text, (int)N, g.nty * g.ntx, tm->n_chunks);
+                             : choose_text_splits(B, H, n_text, (int)N, g.nty * g.ntx, tm->n_entries);
   AttnLaunch a;
   memset(&a, 0, sizeof a);
   a.q = q; a.k = k; a.v = v; a.out = out; a.lse = o.lse_out;
-  a.run_off = tm->run_off; a.runs = tm->runs; a.chunk_off = tm->chunk_off; a.flags = tm->flags;
+  a.tm_offsets = tm->offsets; a.tm_key_tiles = tm->key_tiles; a.tm_flags = tm->flags;
   a.B = B; a.H = H; a.d = d; a.n_text = n_text; a.gh = grid_h; a.gw = grid_w; a.r2 = g.r2;
   a.dtype = o.dtype; a.text_splits = splits;
   if (splits > 1 && n_text > 0) {
@@ -225,23 +224,20 @@ extern "C" int clear_attn_fwd(const void* q, const void* k, const void* v, void*
 }
 
 extern "C" int clear_tile_map_build_device(int grid_h, int grid_w, int r2_max, int tile_h, int tile_w,
-                                           int sub_h, int sub_w, int chunk, uint32_t* run_offsets,
-                                           uint32_t* runs, size_t runs_cap, uint32_t* chunk_offsets,
-                                           uint16_t* flags, size_t flags_cap, size_t* n_runs,
-                                           size_t* n_chunks, void* stream) {
+                                           int sub_h, int sub_w, int key_h, int key_w, uint32_t* offsets,
+                                           uint32_t* key_tiles, uint16_t* flags, size_t cap,
+                                           size_t* n_entries, void* stream) {
   clear_error_reset();
-  int rc = tile_map_validate(grid_h, grid_w, r2_max, tile_h, tile_w, sub_h, sub_w, chunk);
+  int rc = tile_map_validate(grid_h, grid_w, r2_max, tile_h, tile_w, sub_h, sub_w, key_h, key_w);
   if (rc) return rc;
-  if (!n_runs || !n_chunks) return set_error(CLEAR_EINVAL, "n_runs / n_chunks must not be NULL");
-  TileGeom g = make_geom(grid_h, grid_w, r2_max, tile_h, tile_w, sub_h, sub_w, chunk);
-  tile_map_counts(g, n_runs, n_chunks, nullptr, nullptr);
-  if (*n_runs > runs_cap || *n_chunks > flags_cap)
-    return set_error(CLEAR_ENOMEM, "tile map needs %zu runs and %zu chunks (caps %zu, %zu)", *n_runs,
-                     *n_chunks, runs_cap, flags_cap);
-  if (!run_offsets || !chunk_offsets || (*n_runs && !runs) || (*n_chunks && !flags))
+  if (!n_entries) return set_error(CLEAR_EINVAL, "n_entries must not be NULL");
+  TileGeom g = make_geom(grid_h, grid_w, r2_max, tile_h, tile_w, sub_h, sub_w, key_h, key_w);
+  *n_entries = tile_map_count(g);
+  if (*n_entries > cap)
+    return set_error(CLEAR_ENOMEM, "tile map needs %zu entries (capacity %zu)", *n_entries, cap);
+  if (!offsets || (*n_entries && (!key_tiles || !flags)))
     return set_error(CLEAR_EINVAL, "tile map output pointers must not be NULL");
-  if ((size_t)g.nty * g.ntx > (size_t)0x7fffffff) return set_error(CLEAR_EINVAL, "too many tiles");
-  rc = tile_map_build_device_launch(g, run_offsets, runs, chunk_offsets, flags, nullptr, stream);
+  rc = tile_map_build_device_launch(g, offsets, key_tiles, flags, stream);
   if (rc) return rc;
   if (debug_sync_enabled()) {
     hipError_t e = hipStreamSynchronize((hipStream_t)stream);

@@ -1,20 +1,17 @@
-// tile_geom.h -- closed-form geometry of CLEAR's circular window over query tiles.
+// tile_geom.h -- closed-form geometry of CLEAR's circular window over tiles.
 //
 // Shared by the host and the device tile-map builders (which must agree bit for
 // bit).  The window is the image part of CLEAR's mask (pith.science review of
 // arXiv 2412.16112, "Core claim"): key cell (ky, kx) is admitted by query cell
 // (qy, qx) when (qy-ky)^2 + (qx-kx)^2 <= r2.
 //
-// Why the closed forms are exact: for a set of queries Qy x Qx (a rectangle)
-// and keys Ky x Kx (one key row segment, or another rectangle), the squared
-// distance splits as dy^2 + dx^2 with dy depending only on (qy, ky) and dx only
-// on (qx, kx).  Hence the minimum (maximum) of the squared distance over all
-// pairs is the minimum (maximum) of dy^2 plus the minimum (maximum) of dx^2, and
-// those are attained at interval ends.  For one key row ky and a query
-// rectangle [y0, y1] x [x0, x1], some query admits key (ky, kx) iff
-// dymin^2 + dxmin^2 <= r2, i.e. iff kx lies in [x0 - w, x1 + w] with
-// w = isqrt(r2 - dymin^2): the union of the windows on a key row is one
-// interval.
+// Why the closed forms are exact: for a query rectangle Qy x Qx and a key
+// rectangle Ky x Kx, the squared distance of a pair splits as dy^2 + dx^2 with
+// dy depending only on (qy, ky) and dx only on (qx, kx).  The minimum (maximum)
+// of the squared distance over all pairs is therefore the minimum (maximum) of
+// dy^2 plus that of dx^2, and those are attained at interval ends.  So a
+// sub-tile touches a key tile iff dymin^2 + dxmin^2 <= r2, and admits every pair
+// iff dymax^2 + dxmax^2 <= r2.
 #pragma once
 
 #include <stdint.h>
@@ -31,14 +28,16 @@ struct TileGeom {
   int gh, gw, r2;     // grid and squared radius (r2 already clamped to the grid diagonal)
   int th, tw;         // query tile
   int sh, sw;         // sub-tile (one wavefront)
-  int chunk;          // keys per chunk
-  int nty, ntx;       // tiles per column / row
+  int kh, kw;         // key tile
+  int nty, ntx;       // query tiles per column / row
   int nsy, nsx;       // sub-tiles per tile along y / x
+  int nky, nkx;       // key tiles per column / row
   int wmax;           // isqrt(r2) (or -1 when r2 < 0)
 };
 
 CLEAR_HD int imax(int a, int b) { return a > b ? a : b; }
 CLEAR_HD int imin(int a, int b) { return a < b ? a : b; }
+CLEAR_HD int iabs(int a) { return a < 0 ? -a : a; }
 
 // floor(sqrt(x)) for 0 <= x < 2^31, exact.
 CLEAR_HD int isqrt_exact(int x) {
@@ -49,19 +48,21 @@ CLEAR_HD int isqrt_exact(int x) {
   return r;
 }
 
-CLEAR_HD TileGeom make_geom(int gh, int gw, int r2, int th, int tw, int sh, int sw,
-                            int chunk) {
+CLEAR_HD TileGeom make_geom(int gh, int gw, int r2, int th, int tw, int sh, int sw, int kh,
+                            int kw) {
   TileGeom g;
   g.gh = gh; g.gw = gw;
   // Admitting every pair needs at most the grid diagonal; clamping keeps all
   // squares in 32-bit range without changing the mask.
   int64_t diag = (int64_t)(gh - 1) * (gh - 1) + (int64_t)(gw - 1) * (gw - 1);
   g.r2 = (int64_t)r2 > diag ? (int)diag : r2;
-  g.th = th; g.tw = tw; g.sh = sh; g.sw = sw; g.chunk = chunk;
+  g.th = th; g.tw = tw; g.sh = sh; g.sw = sw; g.kh = kh; g.kw = kw;
   g.nty = (gh + th - 1) / th;
   g.ntx = (gw + tw - 1) / tw;
   g.nsy = th / sh;
   g.nsx = tw / sw;
+  g.nky = (gh + kh - 1) / kh;
+  g.nkx = (gw + kw - 1) / kw;
   g.wmax = g.r2 < 0 ? -1 : isqrt_exact(g.r2);
   return g;
 }
@@ -73,47 +74,46 @@ CLEAR_HD void tile_rect(const TileGeom& g, int t, int& y0, int& y1, int& x0, int
   x0 = tx * g.tw; x1 = imin(g.gw, x0 + g.tw) - 1;
 }
 
-// Key rows touched by the tile: [ky_lo, ky_hi]; empty (ky_lo > ky_hi) when r2 < 0.
-// Every key row within wmax of the tile's rows holds a non-empty run, because
-// the run always contains the tile's own columns.
-CLEAR_HD void tile_key_rows(const TileGeom& g, int y0, int y1, int& ky_lo, int& ky_hi) {
-  if (g.wmax < 0) { ky_lo = 0; ky_hi = -1; return; }
-  ky_lo = imax(0, y0 - g.wmax);
-  ky_hi = imin(g.gh - 1, y1 + g.wmax);
+// Candidate key tiles of a query tile: rows [ky_lo, ky_hi] x columns
+// [kx_lo, kx_hi] of key tiles meeting the tile's box widened by wmax (no key
+// outside it can be admitted).  Empty (ky_lo > ky_hi) when r2 < 0.
+CLEAR_HD void candidate_key_tiles(const TileGeom& g, int y0, int y1, int x0, int x1, int& ky_lo,
+                                  int& ky_hi, int& kx_lo, int& kx_hi) {
+  if (g.wmax < 0) { ky_lo = 0; ky_hi = -1; kx_lo = 0; kx_hi = -1; return; }
+  ky_lo = imax(0, y0 - g.wmax) / g.kh;
+  ky_hi = imin(g.gh - 1, y1 + g.wmax) / g.kh;
+  kx_lo = imax(0, x0 - g.wmax) / g.kw;
+  kx_hi = imin(g.gw - 1, x1 + g.wmax) / g.kw;
 }
 
-// Run of admitted columns [a, b] on key row ky for the query rectangle.
-CLEAR_HD void row_run(const TileGeom& g, int y0, int y1, int x0, int x1, int ky, int& a,
-                      int& b) {
-  int dy = imax(0, imax(y0 - ky, ky - y1));
-  int w = isqrt_exact(g.r2 - dy * dy);
-  a = imax(0, x0 - w);
-  b = imin(g.gw - 1, x1 + w);
+// Min / max of |a - b| over a in [a0, a1], b in [b0, b1].
+CLEAR_HD void interval_dist(int a0, int a1, int b0, int b1, int& dmin, int& dmax) {
+  dmin = imax(0, imax(b0 - a1, a0 - b1));
+  dmax = imax(iabs(b1 - a0), iabs(a1 - b0));
 }
 
-// Flags contribution of one piece of a chunk (key row ky, columns [xa, xb])
-// for one sub-tile rectangle (already clipped, non-empty).
-CLEAR_HD void piece_minmax(int ky, int xa, int xb, int sy0, int sy1, int sx0, int sx1,
-                           int& dmin2, int& dmax2) {
-  int dymin = imax(0, imax(sy0 - ky, ky - sy1));
-  int dxmin = imax(0, imax(sx0 - xb, xa - sx1));
-  int dymax = imax(ky - sy0 >= 0 ? ky - sy0 : sy0 - ky, ky - sy1 >= 0 ? ky - sy1 : sy1 - ky);
-  int dxmax = imax(xb - sx0 >= 0 ? xb - sx0 : sx0 - xb, sx1 - xa >= 0 ? sx1 - xa : xa - sx1);
-  dmin2 = dymin * dymin + dxmin * dxmin;
-  dmax2 = dymax * dymax + dxmax * dxmax;
-}
-
-// Clipped rectangle of sub-tile s of the tile whose top-left cell is (y0, x0).
-// Returns false when the sub-tile has no cell on the grid.
-CLEAR_HD bool sub_rect(const TileGeom& g, int ty0, int tx0, int s, int& sy0, int& sy1,
-                       int& sx0, int& sx1) {
-  int sy = s / g.nsx, sx = s - sy * g.nsx;
-  sy0 = ty0 + sy * g.sh;
-  sx0 = tx0 + sx * g.sw;
-  if (sy0 >= g.gh || sx0 >= g.gw) return false;
-  sy1 = imin(g.gh, sy0 + g.sh) - 1;
-  sx1 = imin(g.gw, sx0 + g.sw) - 1;
-  return true;
+// Flags (bit s touched, bit 8+s full) of key tile (kty, ktx) for the query tile
+// whose top-left cell is (ty0, tx0).
+CLEAR_HD unsigned key_tile_flags(const TileGeom& g, int ty0, int tx0, int kty, int ktx) {
+  const int ky0 = kty * g.kh, kx0 = ktx * g.kw;
+  const int ky1 = imin(g.gh, ky0 + g.kh) - 1, kx1 = imin(g.gw, kx0 + g.kw) - 1;
+  const bool on_grid = ky0 + g.kh <= g.gh && kx0 + g.kw <= g.gw;
+  unsigned f = 0;
+  const int nsub = g.nsy * g.nsx;
+  for (int s = 0; s < nsub; ++s) {
+    const int sy = s / g.nsx, sx = s - sy * g.nsx;
+    const int sy0 = ty0 + sy * g.sh, sx0 = tx0 + sx * g.sw;
+    if (sy0 >= g.gh || sx0 >= g.gw) continue;
+    const int sy1 = imin(g.gh, sy0 + g.sh) - 1, sx1 = imin(g.gw, sx0 + g.sw) - 1;
+    int dymin, dymax, dxmin, dxmax;
+    interval_dist(sy0, sy1, ky0, ky1, dymin, dymax);
+    interval_dist(sx0, sx1, kx0, kx1, dxmin, dxmax);
+    if (dymin * dymin + dxmin * dxmin <= g.r2) {
+      f |= 1u << s;
+      if (on_grid && dymax * dymax + dxmax * dxmax <= g.r2) f |= 1u << (8 + s);
+    }
+  }
+  return f;
 }
 
 }  // namespace clear

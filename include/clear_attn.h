@@ -52,13 +52,16 @@ extern "C" {
 #define CLEAR_BF16 0
 #define CLEAR_FP32 1
 
-/* Query tiling of the attention kernels: a workgroup owns a 16 x 8 cell query
- * tile; each of its four wavefronts owns a 4 x 8 sub-tile; keys stream in
- * chunks of 32.  clear_tile_map_build* accept other values (for testing). */
+/* Tiling of the attention kernels: a workgroup owns a 16 x 8 cell query tile;
+ * each of its four wavefronts owns a 4 x 8 sub-tile; image keys stream in 4 x 8
+ * cell key tiles (32 keys), text keys in chunks of 32.  clear_tile_map_build*
+ * accept other tilings (for testing). */
 #define CLEAR_TILE_H 16
 #define CLEAR_TILE_W 8
 #define CLEAR_SUB_H 4
 #define CLEAR_SUB_W 8
+#define CLEAR_KEY_H 4
+#define CLEAR_KEY_W 8
 #define CLEAR_CHUNK 32
 
 /* Largest grid side the kernels accept (grid coordinates travel as 16-bit). */
@@ -106,61 +109,51 @@ int clear_attn_fwd_ex(const void* q, const void* k, const void* v, void* out,
                       const clear_opts* opts, void* stream);
 
 /*
- * clear_tile_map_size -- sizes of the tile map (host, closed form).
- * The tile map lists, for each query tile, the image keys that any of its
- * queries admits (the union of their windows: the mask of the review's
- * "Core claim" restricted to image pairs), as one run of consecutive columns
- * per key row, and cuts that key list into chunks of `chunk` keys.
- *   *n_runs, *n_chunks : totals over all tiles.
+ * clear_tile_map_size -- number of entries of the tile map (host, closed form).
+ * The tile map lists, for each query tile, the key tiles that at least one of
+ * its sub-tiles touches under the mask (the review's "Core claim", image pairs
+ * only), with per-sub-tile flags.
  * Constraints: grid sides 1..CLEAR_MAX_GRID; r2_max >= -1; tile_h, tile_w,
- * sub_h, sub_w >= 1 with sub_h | tile_h, sub_w | tile_w and at most 8
- * sub-tiles per tile; 1 <= chunk <= 4096.
+ * sub_h, sub_w >= 1 with sub_h | tile_h, sub_w | tile_w, tile sides <= 1024 and
+ * at most 8 sub-tiles per tile; key_h, key_w in 1..1024.
  */
 int clear_tile_map_size(int grid_h, int grid_w, int r2_max, int tile_h, int tile_w,
-                        int sub_h, int sub_w, int chunk, size_t* n_runs,
-                        size_t* n_chunks);
+                        int sub_h, int sub_w, int key_h, int key_w, size_t* n_entries);
 
 /*
  * clear_tile_map_build -- build the tile map on the host.
  *
- * Tiles are numbered row-major (t = ty * ceil(grid_w/tile_w) + tx); tile t
- * covers grid rows [ty*tile_h, ty*tile_h + tile_h) and columns
- * [tx*tile_w, tx*tile_w + tile_w), clipped to the grid.  Outputs (host memory,
- * caller-owned):
- *   run_offsets   [ntiles + 1] : runs of tile t are run_offsets[t] .. run_offsets[t+1]-1
- *   runs          [2 * n_runs] : (start, length) pairs; start = ky*grid_w + kx0 is the
- *                                image-token index (text not counted) of the run's first
- *                                key; runs ascend by key row
- *   chunk_offsets [ntiles + 1] : chunks of tile t, in the concatenated key list
- *   flags         [n_chunks]   : bit s = sub-tile s (row-major within the tile) admits
- *                                some pair (query on the grid, key in the chunk); bit 8+s
- *                                = the chunk holds `chunk` keys, sub-tile s has a query
- *                                on the grid and admits every such pair
- * runs_cap / flags_cap are the capacities (in runs / in chunks).  If either is
- * too small, returns CLEAR_ENOMEM with *n_runs / *n_chunks set and nothing
- * written; call with caps 0 to query the sizes.
+ * Query tiles are numbered row-major (t = ty * ceil(grid_w/tile_w) + tx); tile
+ * t covers grid rows [ty*tile_h, ty*tile_h + tile_h) and columns
+ * [tx*tile_w, tx*tile_w + tile_w), clipped to the grid; its sub-tiles are
+ * numbered row-major within it.  Key tiles are numbered row-major the same way
+ * with key_h x key_w cells (id = kty * ceil(grid_w/key_w) + ktx).  Outputs
+ * (host memory, caller-owned):
+ *   offsets   [ntiles + 1] : entries of query tile t are offsets[t] .. offsets[t+1]-1
+ *   key_tiles [n_entries]  : key-tile ids, ascending within a query tile
+ *   flags     [n_entries]  : bit s = sub-tile s admits some pair (query cell of the
+ *                            sub-tile on the grid, key cell of the key tile on the
+ *                            grid); bit 8+s = in addition the key tile lies wholly on
+ *                            the grid and sub-tile s admits every such pair.  A key
+ *                            tile is listed iff some bit 0..7 is set.
+ * cap is the capacity of key_tiles / flags.  If it is too small, returns
+ * CLEAR_ENOMEM with *n_entries set and nothing written (cap 0 queries the size).
  */
 int clear_tile_map_build(int grid_h, int grid_w, int r2_max, int tile_h, int tile_w,
-                         int sub_h, int sub_w, int chunk, uint32_t* run_offsets,
-                         uint32_t* runs, size_t runs_cap, uint32_t* chunk_offsets,
-                         uint16_t* flags, size_t flags_cap, size_t* n_runs,
-                         size_t* n_chunks);
+                         int sub_h, int sub_w, int key_h, int key_w, uint32_t* offsets,
+                         uint32_t* key_tiles, uint16_t* flags, size_t cap,
+                         size_t* n_entries);
 
 /*
- * clear_tile_map_build_device -- same tile map, built by kernels on `stream`
+ * clear_tile_map_build_device -- the same tile map, built by kernels on `stream`
  * into device buffers (same layout and contents, bit for bit, as the host
- * builder).  The sizes are computed on the host first (as clear_tile_map_size);
- * if a capacity is too small it returns CLEAR_ENOMEM with the sizes set and
- * launches nothing.  *n_runs / *n_chunks are host pointers.  Temporary device
- * memory is allocated with stream-ordered allocation and released on the
- * stream.
+ * builder).  The size is computed on the host first; if cap is too small it
+ * returns CLEAR_ENOMEM with *n_entries (a host pointer) set and launches nothing.
  */
 int clear_tile_map_build_device(int grid_h, int grid_w, int r2_max, int tile_h,
-                                int tile_w, int sub_h, int sub_w, int chunk,
-                                uint32_t* run_offsets, uint32_t* runs,
-                                size_t runs_cap, uint32_t* chunk_offsets,
-                                uint16_t* flags, size_t flags_cap, size_t* n_runs,
-                                size_t* n_chunks, void* stream);
+                                int tile_w, int sub_h, int sub_w, int key_h, int key_w,
+                                uint32_t* offsets, uint32_t* key_tiles, uint16_t* flags,
+                                size_t cap, size_t* n_entries, void* stream);
 
 /* Message of the last error raised on the calling thread ("" if none). */
 const char* clear_last_error(void);

@@ -74,21 +74,20 @@ def test_fwd_ex_rejects_bad_arguments(kw, frag):
 
 def test_tile_map_validation_and_size_query():
     L = ca.lib()
-    nr, nc = ctypes.c_size_t(), ctypes.c_size_t()
-    assert L.clear_tile_map_size(0, 4, 1, 16, 8, 4, 8, 32, ctypes.byref(nr), ctypes.byref(nc)) == ca.CLEAR_EINVAL
-    assert L.clear_tile_map_size(8, 8, -2, 16, 8, 4, 8, 32, ctypes.byref(nr), ctypes.byref(nc)) == ca.CLEAR_EINVAL
-    assert L.clear_tile_map_size(8, 8, 4, 16, 8, 3, 8, 32, ctypes.byref(nr), ctypes.byref(nc)) == ca.CLEAR_EINVAL
-    assert L.clear_tile_map_size(8, 8, 4, 16, 8, 2, 4, 32, ctypes.byref(nr), ctypes.byref(nc)) == ca.CLEAR_EINVAL
+    n = ctypes.c_size_t()
+    bad = [(0, 4, 1, 16, 8, 4, 8, 4, 8), (8, 8, -2, 16, 8, 4, 8, 4, 8), (8, 8, 4, 16, 8, 3, 8, 4, 8),
+           (8, 8, 4, 16, 8, 2, 4, 4, 8), (8, 8, 4, 16, 8, 4, 8, 0, 8), (8, 8, 4, 16, 8, 4, 8, 4, 2000)]
+    for args in bad:
+        assert L.clear_tile_map_size(*args, ctypes.byref(n)) == ca.CLEAR_EINVAL, args
+    assert L.clear_tile_map_size(8, 8, 4, 16, 8, 2, 4, 4, 8, ctypes.byref(n)) == ca.CLEAR_EINVAL
     assert "at most 8" in ca.last_error()
-    assert L.clear_tile_map_size(8, 8, 4, 16, 8, 4, 8, 0, ctypes.byref(nr), ctypes.byref(nc)) == ca.CLEAR_EINVAL
-    # caps of zero report the sizes with ENOMEM and write nothing
-    assert L.clear_tile_map_build(64, 64, 64, 16, 8, 4, 8, 32, None, None, 0, None, None, 0,
-                                  ctypes.byref(nr), ctypes.byref(nc)) == ca.CLEAR_ENOMEM
-    assert (nr.value, nc.value) == ca.tile_map_size(64, 64, 64)
-    assert nr.value > 0 and nc.value > 0
-    # the device builder checks capacities on the host before launching anything
-    assert L.clear_tile_map_build_device(64, 64, 64, 16, 8, 4, 8, 32, None, None, 0, None, None, 0,
-                                         ctypes.byref(nr), ctypes.byref(nc), None) == ca.CLEAR_ENOMEM
+    # capacity 0 reports the size with ENOMEM and writes nothing
+    assert L.clear_tile_map_build(64, 64, 64, 16, 8, 4, 8, 4, 8, None, None, None, 0,
+                                  ctypes.byref(n)) == ca.CLEAR_ENOMEM
+    assert n.value == ca.tile_map_size(64, 64, 64) > 0
+    # the device builder checks the capacity on the host before launching anything
+    assert L.clear_tile_map_build_device(64, 64, 64, 16, 8, 4, 8, 4, 8, None, None, None, 0,
+                                         ctypes.byref(n), None) == ca.CLEAR_ENOMEM
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -8,7 +8,7 @@ from oracle import tile_map_bruteforce
 
 
 def _same(lib_tm, ref):
-    for key in ("run_offsets", "runs", "chunk_offsets", "flags"):
+    for key in ("offsets", "key_tiles", "flags"):
         np.testing.assert_array_equal(lib_tm[key], ref[key], err_msg=key)
 
 
@@ -26,13 +26,14 @@ def test_small_grids_all_radii_both_conventions(gh, gw):
         _same(ca.tile_map_build(gh, gw, r2), tile_map_bruteforce(gh, gw, r2))
 
 
-@pytest.mark.parametrize("tiling", [(4, 4, 2, 4, 8), (8, 8, 4, 4, 16), (2, 2, 1, 2, 4), (1, 1, 1, 1, 1),
-                                    (16, 16, 8, 8, 64), (6, 9, 3, 3, 7)])
+@pytest.mark.parametrize("tiling", [(4, 4, 2, 4, 2, 4), (8, 8, 4, 4, 4, 4), (2, 2, 1, 2, 2, 2),
+                                    (1, 1, 1, 1, 1, 1), (16, 16, 8, 8, 8, 8), (6, 9, 3, 3, 5, 2),
+                                    (16, 8, 4, 8, 1, 32), (16, 8, 4, 8, 8, 4)])
 def test_other_tilings(tiling):
-    th, tw, sh, sw, c = tiling
+    th, tw, sh, sw, kh, kw = tiling
     for gh, gw, r2 in [(11, 13, 5), (20, 7, 17), (9, 9, 0), (12, 12, 200)]:
-        _same(ca.tile_map_build(gh, gw, r2, th, tw, sh, sw, c),
-              tile_map_bruteforce(gh, gw, r2, th, tw, sh, sw, c))
+        _same(ca.tile_map_build(gh, gw, r2, th, tw, sh, sw, kh, kw),
+              tile_map_bruteforce(gh, gw, r2, th, tw, sh, sw, kh, kw))
 
 
 @pytest.mark.parametrize("r", [8, 16, 32])
@@ -53,9 +54,7 @@ def test_large_grids_sampled_tiles(g, r):
                        + rng.integers(0, nt, 6).tolist()))
     ref = tile_map_bruteforce(g, g, r * r, tiles=tiles, box=True)
     for i, t in enumerate(tiles):
-        a, b = tm["run_offsets"][t], tm["run_offsets"][t + 1]
-        ra, rb = ref["run_offsets"][i], ref["run_offsets"][i + 1]
-        np.testing.assert_array_equal(tm["runs"][a:b], ref["runs"][ra:rb])
-        a, b = tm["chunk_offsets"][t], tm["chunk_offsets"][t + 1]
-        ra, rb = ref["chunk_offsets"][i], ref["chunk_offsets"][i + 1]
+        a, b = tm["offsets"][t], tm["offsets"][t + 1]
+        ra, rb = ref["offsets"][i], ref["offsets"][i + 1]
+        np.testing.assert_array_equal(tm["key_tiles"][a:b], ref["key_tiles"][ra:rb])
         np.testing.assert_array_equal(tm["flags"][a:b], ref["flags"][ra:rb])

@@ -26,10 +26,11 @@
 // V^T read from row-major V by the LDS transpose load ds_read_b64_tr_b16; fp32
 // uses v_mfma_f32_32x32x2_f32.
 //
-// Pipeline: three LDS stages and two register sets.  Chunk c is fetched from
-// global memory into register set c % 2 two iterations before it is used,
-// written to LDS stage c % 3 one iteration before, and consumed at iteration c;
-// one workgroup barrier per chunk.
+// Pipeline: three LDS stages and one register set.  Chunk c is fetched from
+// global memory into registers two iterations before it is consumed, written
+// to LDS stage c % 3 one iteration before, and its Q.K products are issued one
+// iteration early (overlapping the previous chunk's softmax); one workgroup
+// barrier per chunk.
 //
 // Online softmax in base 2 with a lazily updated reference max: p = 2^(s*c - M)
 // with c = log2(e)/sqrt(d); M is raised only when a row max exceeds M + 8, so
@@ -85,6 +86,7 @@ struct Params {
   const uint16_t* tm_flags;
   int N, n_text, gh, gw, r2;
   int ntiles, ntx, nkx;
+  uint64_t nkx_magic;
   int n_text_blocks, splits, chunks_per_split;
   int n_text_wg, n_text_wg_pad, n_img_wg, BH;
   float scale_log2;
@@ -248,6 +250,7 @@ struct F32 {
 struct KeySource {
   int dense_base, dense_limit, n_dense;
   int n_text, gh, gw, nkx;
+  uint64_t nkx_magic;         // ceil(2^32 / nkx): kt / nkx == (kt * magic) >> 32 here
   const uint32_t* key_tiles;  // the query tile's entries
   const uint16_t* flags;
 };
@@ -281,7 +284,7 @@ __device__ __forceinline__ void gather(RegSet<E>& rs, const KeySource& ks, int j
     const int e = j - ks.n_dense;
     const int kt = (int)ks.key_tiles[e];
     rs.flag = ks.flags[e];
-    const int kty = kt / ks.nkx;
+    const int kty = (int)(((uint64_t)(uint32_t)kt * ks.nkx_magic) >> 32);
     rs.ky0 = kty * kKeyH;
     rs.kx0 = (kt - kty * ks.nkx) * kKeyW;
     for (int r = 0; r < E::kKIters; ++r) {
@@ -318,45 +321,53 @@ struct SoftmaxState {
   float M, L;
 };
 
-// Consume one chunk from LDS stage `st` (one wavefront).
+// What one wavefront does with chunk j: whether it computes it at all, and
+// which mask applies (tail of a dense range, or the circular window).
+struct ChunkInfo {
+  bool active;
+  bool coord;
+  int tail;  // dense chunk: positions >= tail are masked
+  int ky0, kx0;
+};
+
 template <class E>
-__device__ __forceinline__ void compute_chunk(E& eng, SoftmaxState& sm, const char* st, int j,
-                                              const KeySource& ks, int lane, int wave, int qy,
-                                              int qx, int r2, float scale_log2) {
-  const int g = lane >> 5;
-  int tail = 32;  // dense chunk: positions >= tail are masked
-  bool coord_mask = false;
-  int ky0 = 0, kx0 = 0;
+__device__ __forceinline__ ChunkInfo chunk_info(const char* st, int j, const KeySource& ks, int wave) {
+  ChunkInfo c{true, false, 32, 0, 0};
   if (j < ks.n_dense) {
-    const int rem_keys = ks.dense_limit - (ks.dense_base + j * kChunk);
-    tail = rem_keys < 32 ? rem_keys : 32;
+    const int rem = ks.dense_limit - (ks.dense_base + j * kChunk);
+    c.tail = rem < 32 ? rem : 32;
   } else {
     const int* m = (const int*)(st + E::kMOff);
     const unsigned f = (unsigned)m[0];
-    if (!((f >> wave) & 1u)) return;
-    coord_mask = !((f >> (8 + wave)) & 1u);
-    ky0 = m[1];
-    kx0 = m[2];
+    c.active = (f >> wave) & 1u;
+    c.coord = !((f >> (8 + wave)) & 1u);
+    c.ky0 = m[1];
+    c.kx0 = m[2];
   }
+  return c;
+}
 
-  f32x16_t s;
-  eng.qk(st, lane, s);
-
-  if (tail < 32) {
+// Mask, online softmax and P.V for the logits s of one chunk (one wavefront).
+template <class E>
+__device__ __forceinline__ void softmax_pv(E& eng, SoftmaxState& sm, const char* st, f32x16_t& s,
+                                           const ChunkInfo& c, const KeySource& ks, int lane,
+                                           int qy, int qx, int r2, float scale_log2) {
+  const int g = lane >> 5;
+  if (c.tail < 32) {
     for (int i = 0; i < 16; ++i)
-      if (acc_row(i, g) >= tail) s[i] = -__builtin_inff();
-  } else if (coord_mask) {
+      if (acc_row(i, g) >= c.tail) s[i] = -__builtin_inff();
+  } else if (c.coord) {
     // Register i of lane group g holds key cell (ky0 + i/4, kx0 + 4g + i%4) of
     // the key tile; admitted iff dx^2 <= r2 - dy^2 with both cells on the grid.
     int lim[4], dxx[4];
     for (int a = 0; a < 4; ++a) {
-      const int dy = qy - ky0 - a;
-      lim[a] = ky0 + a < ks.gh ? r2 - dy * dy : -1;
+      const int dy = qy - c.ky0 - a;
+      lim[a] = c.ky0 + a < ks.gh ? r2 - __mul24(dy, dy) : -1;
     }
     for (int b = 0; b < 4; ++b) {
-      const int kx = kx0 + 4 * g + b;
+      const int kx = c.kx0 + 4 * g + b;
       const int dx = qx - kx;
-      dxx[b] = kx < ks.gw ? dx * dx : 0x7fffffff;
+      dxx[b] = kx < ks.gw ? __mul24(dx, dx) : 0x7fffffff;
     }
     for (int i = 0; i < 16; ++i)
       if (dxx[i & 3] > lim[i >> 2]) s[i] = -__builtin_inff();
@@ -405,6 +416,7 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
   ks.gh = p.gh;
   ks.gw = p.gw;
   ks.nkx = p.nkx;
+  ks.nkx_magic = p.nkx_magic;
   ks.key_tiles = p.tm_key_tiles;
   ks.flags = p.tm_flags;
   int n_chunks;
@@ -458,35 +470,58 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
   const bool wave_active = __ballot(qvalid) != 0ull;
   SoftmaxState sm{kMInit, 0.0f};
 
-  // ---- pipelined main loop: chunk c in register set c % 2, LDS stage c % 3
-  RegSet<E> s0, s1;
+  // ---- pipelined main loop.  Chunk c is fetched into registers at iteration
+  // c - 2, written to LDS stage c % 3 at iteration c - 1 and consumed at
+  // iteration c.  After the barrier of iteration j, chunks j and j + 1 are both
+  // in LDS: the wavefront issues the Q.K products of chunk j + 1 before the
+  // softmax and P.V of chunk j, so matrix-core work overlaps the softmax.
+  RegSet<E> rs;
+  f32x16_t sa, sb;  // logits of the current / next chunk (alternating)
   const int n = n_chunks;
-  if (n > 0) gather(s0, ks, 0, kbase, vbase);
-  if (n > 1) gather(s1, ks, 1, kbase, vbase);
-  if (n > 0) lstore(smem, s0);
-  if (n > 2) gather(s0, ks, 2, kbase, vbase);
-  int st_cur = 0;  // stage of chunk j
+  // LDS stages of chunks j, j + 1, j + 2 (rotated each iteration)
+  char* st0 = smem;
+  char* st1 = smem + E::kStage;
+  char* st2 = smem + 2 * E::kStage;
+  if (n > 0) {
+    gather(rs, ks, 0, kbase, vbase);
+    lstore(st0, rs);
+  }
+  if (n > 1) gather(rs, ks, 1, kbase, vbase);
+  __syncthreads();
+  ChunkInfo ca{false, false, 32, 0, 0}, cb{false, false, 32, 0, 0};
+  if (n > 0 && wave_active) {
+    ca = chunk_info<E>(st0, 0, ks, wave);
+    if (ca.active) eng.qk(st0, lane, sa);
+  }
   for (int j = 0; j < n; j += 2) {
-    {
-      const int st_next = st_cur == kStages - 1 ? 0 : st_cur + 1;
-      if (j + 1 < n) lstore(smem + st_next * E::kStage, s1);
-      if (j + 3 < n) gather(s1, ks, j + 3, kbase, vbase);
-      __syncthreads();
-      if (wave_active)
-        compute_chunk(eng, sm, smem + st_cur * E::kStage, j, ks, lane, wave, qy, qx, p.r2,
-                      p.scale_log2);
-      st_cur = st_next;
+    // chunk j in (sa, ca, st0); chunk j + 1 goes to (sb, cb, st1)
+    if (j + 1 < n) lstore(st1, rs);
+    if (j + 2 < n) gather(rs, ks, j + 2, kbase, vbase);
+    __syncthreads();
+    if (wave_active) {
+      if (j + 1 < n) {
+        cb = chunk_info<E>(st1, j + 1, ks, wave);
+        if (cb.active) eng.qk(st1, lane, sb);
+      }
+      if (ca.active) softmax_pv(eng, sm, st0, sa, ca, ks, lane, qy, qx, p.r2, p.scale_log2);
     }
-    if (j + 1 < n) {
-      const int st_next = st_cur == kStages - 1 ? 0 : st_cur + 1;
-      if (j + 2 < n) lstore(smem + st_next * E::kStage, s0);
-      if (j + 4 < n) gather(s0, ks, j + 4, kbase, vbase);
-      __syncthreads();
-      if (wave_active)
-        compute_chunk(eng, sm, smem + st_cur * E::kStage, j + 1, ks, lane, wave, qy, qx, p.r2,
-                      p.scale_log2);
-      st_cur = st_next;
+    if (j + 1 >= n) break;
+    // chunk j + 1 in (sb, cb, st1); chunk j + 2 goes to (sa, ca, st2)
+    if (j + 2 < n) lstore(st2, rs);
+    if (j + 3 < n) gather(rs, ks, j + 3, kbase, vbase);
+    __syncthreads();
+    if (wave_active) {
+      if (j + 2 < n) {
+        ca = chunk_info<E>(st2, j + 2, ks, wave);
+        if (ca.active) eng.qk(st2, lane, sa);
+      }
+      if (cb.active) softmax_pv(eng, sm, st1, sb, cb, ks, lane, qy, qx, p.r2, p.scale_log2);
     }
+    // stages of chunks j + 2, j + 3, j + 4
+    char* t = st0;
+    st0 = st2;
+    st2 = st1;
+    st1 = t;
   }
 
   // ---- epilogue
@@ -576,6 +611,8 @@ int attn_launch(const AttnLaunch& a, void* stream) {
   p.ntx = (a.gw + kTileW - 1) / kTileW;
   p.ntiles = ((a.gh + kTileH - 1) / kTileH) * p.ntx;
   p.nkx = (a.gw + kKeyW - 1) / kKeyW;
+  // exact for kt * nkx < 2^32 (kt < 2^21 and nkx <= 1024 on grids up to 8192^2)
+  p.nkx_magic = ((1ull << 32) + (uint64_t)p.nkx - 1) / (uint64_t)p.nkx;
   p.BH = a.B * a.H;
   p.n_text_blocks = (a.n_text + kTextQ - 1) / kTextQ;
   const int nall = (p.N + kChunk - 1) / kChunk;

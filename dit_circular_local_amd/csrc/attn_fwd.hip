@@ -26,11 +26,11 @@
 // V^T read from row-major V by the LDS transpose load ds_read_b64_tr_b16; fp32
 // uses v_mfma_f32_32x32x2_f32.
 //
-// Pipeline: three LDS stages and one register set.  Chunk c is fetched from
-// global memory into registers two iterations before it is consumed, written
-// to LDS stage c % 3 one iteration before, and its Q.K products are issued one
-// iteration early (overlapping the previous chunk's softmax); one workgroup
-// barrier per chunk.
+// Pipeline: three LDS stages and two register sets.  Chunk c is fetched from
+// global memory into register set c % 2 three iterations before it is
+// consumed, written to LDS stage c % 3 one iteration before, and its Q.K
+// products are issued one iteration early (overlapping the previous chunk's
+// softmax); one workgroup barrier per chunk.
 //
 // Online softmax in base 2 with a lazily updated reference max: p = 2^(s*c - M)
 // with c = log2(e)/sqrt(d); M is raised only when a row max exceeds M + 8, so
@@ -119,8 +119,7 @@ struct Bf16 {
   static constexpr int kRowV = D * 2 + 64;
   static constexpr int kKOff = 0;
   static constexpr int kVOff = kChunk * kRowK;
-  static constexpr int kMOff = kVOff + kChunk * kRowV;   // chunk meta: flags, ky0, kx0
-  static constexpr int kStage = kMOff + 16;
+  static constexpr int kStage = kVOff + kChunk * kRowV;
   static constexpr int kKIters = kChunk * kPPR / kThreads;
   static constexpr int kKK = D / 16;
   static constexpr int kNB = D / 32;
@@ -147,6 +146,23 @@ struct Bf16 {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q[kk], s, 0, 0, 0);
     }
   }
+  // Probabilities as the B operand of P.V (bf16, registers 8t .. 8t+7 in
+  // operand t) and their sum, taken over the rounded values P.V uses.
+  struct Probs {
+    bf16x8_t b[2];
+  };
+  __device__ static float probs(const f32x16_t& e, Probs& pr) {
+    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+    float l = 0.0f;
+    for (int t = 0; t < 2; ++t)
+      for (int j = 0; j < 4; ++j) {
+        const bf16x2_t h = __builtin_convertvector(f32x2_t{e[8 * t + 2 * j], e[8 * t + 2 * j + 1]}, bf16x2_t);
+        pr.b[t][2 * j] = h[0];
+        pr.b[t][2 * j + 1] = h[1];
+        l = __builtin_amdgcn_fdot2_f32_bf16(h, one, l, false);
+      }
+    return l;
+  }
   // O^T += V^T P^T.  The A operand (lane l: d = 32*nb + l % 32, eight keys of
   // lane group g = l / 32) comes from two transpose loads: in each 16-lane group,
   // lane i receives element i % 4 of the 8-byte rows addressed by lanes i/4,
@@ -156,25 +172,19 @@ struct Bf16 {
   // 16t + 8h + 4g + e (e = 0..3) at d = 32nb + l % 32, which are the keys of
   // accumulator registers 8t + 4h + e (acc_row) whose probabilities the B
   // operand carries.
-  __device__ void pv(const char* st, int lane, const f32x16_t& p) {
+  __device__ void pv(const char* st, int lane, const Probs& pr) {
     const int g = lane >> 5;
     const int s = lane & 15;
     const int half = (lane >> 4) & 1;
     const char* vb = st + kVOff + (4 * g + (s >> 2)) * kRowV + (16 * half + 4 * (s & 3)) * 2;
     for (int t = 0; t < 2; ++t) {
-      bf16x8_t b;
-      for (int j = 0; j < 4; ++j) {
-        bf16x2_t h = __builtin_convertvector(f32x2_t{p[8 * t + 2 * j], p[8 * t + 2 * j + 1]}, bf16x2_t);
-        b[2 * j] = h[0];
-        b[2 * j + 1] = h[1];
-      }
       for (int nb = 0; nb < kNB; ++nb) {
         const char* a0 = vb + 16 * t * kRowV + nb * 64;
         s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds_char_t*)const_cast<char*>(a0));
         s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4_t*)(lds_char_t*)const_cast<char*>(a0 + 8 * kRowV));
         s16x8_t w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), b, o[nb], 0, 0, 0);
+        o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pr.b[t], o[nb], 0, 0, 0);
       }
     }
   }
@@ -198,8 +208,7 @@ struct F32 {
   static constexpr int kRowV = D * 4 + 16;
   static constexpr int kKOff = 0;
   static constexpr int kVOff = kChunk * kRowK;
-  static constexpr int kMOff = kVOff + kChunk * kRowV;   // chunk meta: flags, ky0, kx0
-  static constexpr int kStage = kMOff + 16;
+  static constexpr int kStage = kVOff + kChunk * kRowV;
   static constexpr int kKIters = kChunk * kPPR / kThreads;
   static constexpr int kHalf = D / 2;   // d values per lane group in Q.K
   static constexpr int kNB = D / 32;
@@ -227,7 +236,17 @@ struct F32 {
         s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], q[4 * s4 + e], s, 0, 0, 0);
     }
   }
-  __device__ void pv(const char* st, int lane, const f32x16_t& p) {
+  struct Probs {
+    f32x16_t p;
+  };
+  __device__ static float probs(const f32x16_t& e, Probs& pr) {
+    float l = 0.0f;
+    for (int i = 0; i < 16; ++i) l += e[i];
+    pr.p = e;
+    return l;
+  }
+  __device__ void pv(const char* st, int lane, const Probs& pr) {
+    const f32x16_t& p = pr.p;
     const int g = lane >> 5;
     for (int u = 0; u < 16; ++u) {
       const float* vr = (const float*)(st + kVOff + acc_row(u, g) * kRowV) + (lane & 31);
@@ -255,6 +274,17 @@ struct KeySource {
   const uint16_t* flags;
 };
 
+// Byte offsets (from the chunk's first key) of the 16-byte pieces this thread
+// moves: inside a key tile that lies on the grid, and inside a dense range.
+template <class E>
+struct ThreadOffsets {
+  uint32_t tile[E::kKIters];
+  uint32_t dense[E::kKIters];
+};
+
+__device__ __forceinline__ int kpos_of(int r, int ppr) { return (threadIdx.x + r * kThreads) / ppr; }
+__device__ __forceinline__ int kcol_of(int r, int ppr) { return (threadIdx.x + r * kThreads) % ppr; }
+
 // One chunk in flight in registers: K and V pieces of this thread, and the
 // chunk's flags and key-tile origin (uniform).
 template <class E>
@@ -265,40 +295,51 @@ struct RegSet {
   int ky0, kx0;
 };
 
-__device__ __forceinline__ int kpos_of(int r, int ppr) { return (threadIdx.x + r * kThreads) / ppr; }
-__device__ __forceinline__ int kcol_of(int r, int ppr) { return (threadIdx.x + r * kThreads) % ppr; }
-
 template <class E>
 __device__ __forceinline__ void gather(RegSet<E>& rs, const KeySource& ks, int j, const char* kbase,
-                                       const char* vbase) {
-  int tok[E::kKIters];
+                                       const char* vbase, const ThreadOffsets<E>& to) {
+  uint32_t off[E::kKIters];
+  size_t base;
   if (j < ks.n_dense) {
+    const int t0 = ks.dense_base + j * kChunk;
     rs.flag = 0;
     rs.ky0 = 0;
     rs.kx0 = 0;
-    for (int r = 0; r < E::kKIters; ++r) {
-      const int t = ks.dense_base + j * kChunk + kpos_of(r, E::kPPR);
-      tok[r] = t < ks.dense_limit ? t : ks.dense_limit - 1;
+    base = (size_t)t0 * E::kRowBytes;
+    if (t0 + kChunk <= ks.dense_limit) {
+      for (int r = 0; r < E::kKIters; ++r) off[r] = to.dense[r];
+    } else {
+      // positions past the range load its last key; the tail mask drops them
+      for (int r = 0; r < E::kKIters; ++r) {
+        const int t = min(t0 + kpos_of(r, E::kPPR), ks.dense_limit - 1) - t0;
+        off[r] = (uint32_t)(t * E::kRowBytes + kcol_of(r, E::kPPR) * 16);
+      }
     }
   } else {
     const int e = j - ks.n_dense;
-    const int kt = (int)ks.key_tiles[e];
+    const uint32_t kt = ks.key_tiles[e];
     rs.flag = ks.flags[e];
-    const int kty = (int)(((uint64_t)(uint32_t)kt * ks.nkx_magic) >> 32);
+    const int kty = (int)(((uint64_t)kt * ks.nkx_magic) >> 32);
     rs.ky0 = kty * kKeyH;
-    rs.kx0 = (kt - kty * ks.nkx) * kKeyW;
-    for (int r = 0; r < E::kKIters; ++r) {
-      const int p = kpos_of(r, E::kPPR);
-      // cells past the grid edge load an in-grid row; the mask drops them
-      const int ky = min(rs.ky0 + (p >> 3), ks.gh - 1);
-      const int kx = min(rs.kx0 + (p & 7), ks.gw - 1);
-      tok[r] = ks.n_text + ky * ks.gw + kx;
+    rs.kx0 = ((int)kt - kty * ks.nkx) * kKeyW;
+    base = (size_t)(ks.n_text + rs.ky0 * ks.gw + rs.kx0) * E::kRowBytes;
+    if (rs.ky0 + kKeyH <= ks.gh && rs.kx0 + kKeyW <= ks.gw) {
+      for (int r = 0; r < E::kKIters; ++r) off[r] = to.tile[r];
+    } else {
+      // cells past the grid edge load an in-grid key; the mask drops them
+      for (int r = 0; r < E::kKIters; ++r) {
+        const int p = kpos_of(r, E::kPPR);
+        const int a = min(rs.ky0 + (p >> 3), ks.gh - 1) - rs.ky0;
+        const int c = min(rs.kx0 + (p & 7), ks.gw - 1) - rs.kx0;
+        off[r] = (uint32_t)((a * ks.gw + c) * E::kRowBytes + kcol_of(r, E::kPPR) * 16);
+      }
     }
   }
+  const char* kb = kbase + base;
+  const char* vb = vbase + base;
   for (int r = 0; r < E::kKIters; ++r) {
-    const size_t off = (size_t)tok[r] * E::kRowBytes + kcol_of(r, E::kPPR) * 16;
-    rs.k[r] = *(const u32x4_t*)(kbase + off);
-    rs.v[r] = *(const u32x4_t*)(vbase + off);
+    rs.k[r] = *(const u32x4_t*)(kb + off[r]);
+    rs.v[r] = *(const u32x4_t*)(vb + off[r]);
   }
 }
 
@@ -308,12 +349,6 @@ __device__ __forceinline__ void lstore(char* st, const RegSet<E>& rs) {
     const int pos = kpos_of(r, E::kPPR), col = kcol_of(r, E::kPPR);
     *(u32x4_t*)(st + E::kKOff + pos * E::kRowK + col * 16) = rs.k[r];
     *(u32x4_t*)(st + E::kVOff + pos * E::kRowV + col * 16) = rs.v[r];
-  }
-  if (threadIdx.x == 0) {
-    int* m = (int*)(st + E::kMOff);
-    m[0] = (int)rs.flag;
-    m[1] = rs.ky0;
-    m[2] = rs.kx0;
   }
 }
 
@@ -326,30 +361,29 @@ struct SoftmaxState {
 struct ChunkInfo {
   bool active;
   bool coord;
-  int tail;  // dense chunk: positions >= tail are masked
+  bool inside;  // key tile wholly on the grid
+  int tail;     // dense chunk: positions >= tail are masked
   int ky0, kx0;
 };
 
 template <class E>
-__device__ __forceinline__ ChunkInfo chunk_info(const char* st, int j, const KeySource& ks, int wave) {
-  ChunkInfo c{true, false, 32, 0, 0};
+__device__ __forceinline__ ChunkInfo chunk_info(const RegSet<E>& rs, int j, const KeySource& ks,
+                                                int wave) {
+  ChunkInfo c{true, false, true, 32, rs.ky0, rs.kx0};
   if (j < ks.n_dense) {
     const int rem = ks.dense_limit - (ks.dense_base + j * kChunk);
     c.tail = rem < 32 ? rem : 32;
   } else {
-    const int* m = (const int*)(st + E::kMOff);
-    const unsigned f = (unsigned)m[0];
-    c.active = (f >> wave) & 1u;
-    c.coord = !((f >> (8 + wave)) & 1u);
-    c.ky0 = m[1];
-    c.kx0 = m[2];
+    c.active = (rs.flag >> wave) & 1u;
+    c.coord = !((rs.flag >> (8 + wave)) & 1u);
+    c.inside = rs.ky0 + kKeyH <= ks.gh && rs.kx0 + kKeyW <= ks.gw;
   }
   return c;
 }
 
 // Mask, online softmax and P.V for the logits s of one chunk (one wavefront).
 template <class E>
-__device__ __forceinline__ void softmax_pv(E& eng, SoftmaxState& sm, const char* st, f32x16_t& s,
+__device__ __forceinline__ void softmax_pv(E& eng, SoftmaxState& sm, const char* st, f32x16_t s,
                                            const ChunkInfo& c, const KeySource& ks, int lane,
                                            int qy, int qx, int r2, float scale_log2) {
   const int g = lane >> 5;
@@ -360,14 +394,14 @@ __device__ __forceinline__ void softmax_pv(E& eng, SoftmaxState& sm, const char*
     // Register i of lane group g holds key cell (ky0 + i/4, kx0 + 4g + i%4) of
     // the key tile; admitted iff dx^2 <= r2 - dy^2 with both cells on the grid.
     int lim[4], dxx[4];
-    for (int a = 0; a < 4; ++a) {
-      const int dy = qy - c.ky0 - a;
-      lim[a] = c.ky0 + a < ks.gh ? r2 - __mul24(dy, dy) : -1;
-    }
-    for (int b = 0; b < 4; ++b) {
-      const int kx = c.kx0 + 4 * g + b;
-      const int dx = qx - kx;
-      dxx[b] = kx < ks.gw ? __mul24(dx, dx) : 0x7fffffff;
+    const int dy0 = qy - c.ky0, dx0 = qx - c.kx0 - 4 * g;
+    for (int a = 0; a < 4; ++a) lim[a] = r2 - __mul24(dy0 - a, dy0 - a);
+    for (int b = 0; b < 4; ++b) dxx[b] = __mul24(dx0 - b, dx0 - b);
+    if (!c.inside) {
+      for (int a = 0; a < 4; ++a)
+        if (c.ky0 + a >= ks.gh) lim[a] = -1;
+      for (int b = 0; b < 4; ++b)
+        if (c.kx0 + 4 * g + b >= ks.gw) dxx[b] = 0x7fffffff;
     }
     for (int i = 0; i < 16; ++i)
       if (dxx[i & 3] > lim[i >> 2]) s[i] = -__builtin_inff();
@@ -386,14 +420,11 @@ __device__ __forceinline__ void softmax_pv(E& eng, SoftmaxState& sm, const char*
       for (int i = 0; i < 16; ++i) eng.o[nb][i] *= alpha;
     sm.M = Mn;
   }
-  float lsum = 0.0f;
-  for (int i = 0; i < 16; ++i) {
-    const float e = __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -sm.M));
-    s[i] = e;
-    lsum += e;
-  }
-  sm.L += lsum;
-  eng.pv(st, lane, s);
+  f32x16_t e;
+  for (int i = 0; i < 16; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -sm.M));
+  typename E::Probs pr;
+  sm.L += E::probs(e, pr);
+  eng.pv(st, lane, pr);
 }
 
 template <class E>
@@ -401,7 +432,7 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
   __shared__ __attribute__((aligned(16))) char smem[kStages * E::kStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5;
   const int qi = lane & 31;
   const int bid = blockIdx.x;
@@ -464,6 +495,13 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
   const char* kbase = p.k + head_off;
   const char* vbase = p.v + head_off;
 
+  ThreadOffsets<E> toff;
+  for (int r = 0; r < E::kKIters; ++r) {
+    const int pp = kpos_of(r, E::kPPR), col = kcol_of(r, E::kPPR);
+    toff.tile[r] = (uint32_t)((((pp >> 3) * p.gw) + (pp & 7)) * E::kRowBytes + col * 16);
+    toff.dense[r] = (uint32_t)(pp * E::kRowBytes + col * 16);
+  }
+
   E eng;
   eng.load_q(p.q + head_off + (size_t)(qvalid ? qtok : 0) * E::kRowBytes, qvalid, g);
   eng.zero_o();
@@ -475,46 +513,45 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
   // iteration c.  After the barrier of iteration j, chunks j and j + 1 are both
   // in LDS: the wavefront issues the Q.K products of chunk j + 1 before the
   // softmax and P.V of chunk j, so matrix-core work overlaps the softmax.
-  RegSet<E> rs;
-  f32x16_t sa, sb;  // logits of the current / next chunk (alternating)
+  RegSet<E> ra, rb;  // chunks in flight: even chunks in ra, odd chunks in rb
+  f32x16_t sa, sb;   // logits of the current / next chunk (alternating)
   const int n = n_chunks;
-  // LDS stages of chunks j, j + 1, j + 2 (rotated each iteration)
+  // LDS stages of chunks j, j + 1, j + 2 (rotated every two iterations)
   char* st0 = smem;
   char* st1 = smem + E::kStage;
   char* st2 = smem + 2 * E::kStage;
+  ChunkInfo ca{false, false, true, 32, 0, 0}, cb{false, false, true, 32, 0, 0};
+  if (n > 0) gather(ra, ks, 0, kbase, vbase, toff);
+  if (n > 1) gather(rb, ks, 1, kbase, vbase, toff);
   if (n > 0) {
-    gather(rs, ks, 0, kbase, vbase);
-    lstore(st0, rs);
+    lstore(st0, ra);
+    ca = chunk_info(ra, 0, ks, wave);
   }
-  if (n > 1) gather(rs, ks, 1, kbase, vbase);
+  if (n > 2) gather(ra, ks, 2, kbase, vbase, toff);
   __syncthreads();
-  ChunkInfo ca{false, false, 32, 0, 0}, cb{false, false, 32, 0, 0};
-  if (n > 0 && wave_active) {
-    ca = chunk_info<E>(st0, 0, ks, wave);
-    if (ca.active) eng.qk(st0, lane, sa);
-  }
+  if (n > 0 && wave_active && ca.active) eng.qk(st0, lane, sa);
   for (int j = 0; j < n; j += 2) {
     // chunk j in (sa, ca, st0); chunk j + 1 goes to (sb, cb, st1)
-    if (j + 1 < n) lstore(st1, rs);
-    if (j + 2 < n) gather(rs, ks, j + 2, kbase, vbase);
+    if (j + 1 < n) {
+      lstore(st1, rb);
+      cb = chunk_info(rb, j + 1, ks, wave);
+    }
+    if (j + 3 < n) gather(rb, ks, j + 3, kbase, vbase, toff);
     __syncthreads();
     if (wave_active) {
-      if (j + 1 < n) {
-        cb = chunk_info<E>(st1, j + 1, ks, wave);
-        if (cb.active) eng.qk(st1, lane, sb);
-      }
+      if (j + 1 < n && cb.active) eng.qk(st1, lane, sb);
       if (ca.active) softmax_pv(eng, sm, st0, sa, ca, ks, lane, qy, qx, p.r2, p.scale_log2);
     }
     if (j + 1 >= n) break;
     // chunk j + 1 in (sb, cb, st1); chunk j + 2 goes to (sa, ca, st2)
-    if (j + 2 < n) lstore(st2, rs);
-    if (j + 3 < n) gather(rs, ks, j + 3, kbase, vbase);
+    if (j + 2 < n) {
+      lstore(st2, ra);
+      ca = chunk_info(ra, j + 2, ks, wave);
+    }
+    if (j + 4 < n) gather(ra, ks, j + 4, kbase, vbase, toff);
     __syncthreads();
     if (wave_active) {
-      if (j + 2 < n) {
-        ca = chunk_info<E>(st2, j + 2, ks, wave);
-        if (ca.active) eng.qk(st2, lane, sa);
-      }
+      if (j + 2 < n && ca.active) eng.qk(st2, lane, sa);
       if (cb.active) softmax_pv(eng, sm, st1, sb, cb, ks, lane, qy, qx, p.r2, p.scale_log2);
     }
     // stages of chunks j + 2, j + 3, j + 4

@@ -129,14 +129,21 @@ struct Bf16 {
   bf16x8_t q[kKK];
   f32x16_t o[kNB];
 
+  // qrow is always a valid row (invalid queries read row 0 and are zeroed), so
+  // every lane issues the same loads.
   __device__ void load_q(const char* qrow, bool valid, int g) {
     for (int kk = 0; kk < kKK; ++kk) {
-      u32x4_t x = valid ? *(const u32x4_t*)(qrow + (16 * kk + 8 * g) * 2) : u32x4_t{0, 0, 0, 0};
-      q[kk] = __builtin_bit_cast(bf16x8_t, x);
+      const u32x4_t x = *(const u32x4_t*)(qrow + (16 * kk + 8 * g) * 2);
+      q[kk] = __builtin_bit_cast(bf16x8_t, valid ? x : u32x4_t{0, 0, 0, 0});
     }
   }
   __device__ void zero_o() {
     for (int nb = 0; nb < kNB; ++nb) o[nb] = f32x16_t{};
+  }
+  // Waits for the Q loads here, once, so that no wait for them is left
+  // inside the chunk loop (where it would also wait for the prefetches).
+  __device__ void settle_q() {
+    for (int kk = 0; kk < kKK; ++kk) asm volatile("" ::"v"(q[kk]));
   }
   __device__ void qk(const char* st, int lane, f32x16_t& s) const {
     const char* kb = st + kKOff + (lane & 31) * kRowK + (lane >> 5) * 16;
@@ -220,12 +227,15 @@ struct F32 {
 
   __device__ void load_q(const char* qrow, bool valid, int g) {
     for (int s4 = 0; s4 < kHalf / 4; ++s4) {
-      f32x4_t x = valid ? *(const f32x4_t*)(qrow + (kHalf * g + 4 * s4) * 4) : f32x4_t{0, 0, 0, 0};
-      for (int e = 0; e < 4; ++e) q[4 * s4 + e] = x[e];
+      const f32x4_t x = *(const f32x4_t*)(qrow + (kHalf * g + 4 * s4) * 4);
+      for (int e = 0; e < 4; ++e) q[4 * s4 + e] = valid ? x[e] : 0.0f;
     }
   }
   __device__ void zero_o() {
     for (int nb = 0; nb < kNB; ++nb) o[nb] = f32x16_t{};
+  }
+  __device__ void settle_q() {
+    for (int i = 0; i < kHalf; ++i) asm volatile("" ::"v"(q[i]));
   }
   __device__ void qk(const char* st, int lane, f32x16_t& s) const {
     const char* kb = st + kKOff + (lane & 31) * kRowK + (lane >> 5) * kHalf * 4;
@@ -266,12 +276,16 @@ struct F32 {
 // tile, or a key range of a text workgroup); chunk n_dense + e is the e-th key
 // tile the tile map lists for the query tile, position p = 8a + c being its
 // key cell (ky0 + a, kx0 + c).
+typedef __attribute__((address_space(4))) const uint32_t const_u32_t;
+
 struct KeySource {
   int dense_base, dense_limit, n_dense;
   int n_text, gh, gw, nkx;
-  uint64_t nkx_magic;         // ceil(2^32 / nkx): kt / nkx == (kt * magic) >> 32 here
-  const uint32_t* key_tiles;  // the query tile's entries
-  const uint16_t* flags;
+  uint64_t nkx_magic;    // ceil(2^32 / nkx): kt / nkx == (kt * magic) >> 32 here
+  int e0;                // the query tile's first tile-map entry
+  int n_tok;             // tokens per head (N)
+  const_u32_t* key_tiles;  // whole tile map, read through the scalar cache
+  const_u32_t* flags32;    // u16 flags, two per word
 };
 
 // Byte offsets (from the chunk's first key) of the 16-byte pieces this thread
@@ -295,60 +309,62 @@ struct RegSet {
   int ky0, kx0;
 };
 
+// Buffer resource over `bytes` bytes from a uniform address (gfx9 resource
+// word 3).  Loads at offsets >= bytes return zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_rsrc(const char* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Fetch chunk j into registers.  The chunk's first key row is uniform, so the
+// buffer resources carry it in scalar registers and every thread adds one of
+// two loop-invariant piece offsets (dense range, or key tile).  Pieces that fall
+// outside the chunk's keys need no special path: past the end of the head the
+// resource bound returns zeros; past the grid's right edge they read the next
+// row's keys; past a dense range's limit, the following tokens.  All of these
+// are finite and removed by the mask.
+template <int PATH, class E>
+__device__ __forceinline__ void load_chunk(RegSet<E>& rs, const KeySource& ks, const char* kbase,
+                                           const char* vbase, int tok0, const uint32_t* off) {
+  const size_t base = (size_t)tok0 * E::kRowBytes;
+  const size_t left = (size_t)(ks.n_tok - tok0) * E::kRowBytes;
+  const uint32_t bytes = left < 0x7fffffffu ? (uint32_t)left : 0x7fffffffu;
+  const __amdgpu_buffer_rsrc_t rk = byte_rsrc(kbase + base, bytes), rv = byte_rsrc(vbase + base, bytes);
+  for (int r = 0; r < E::kKIters; ++r) {
+    rs.k[r] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)off[r], 0, 0));
+    rs.v[r] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)off[r], 0, 0));
+  }
+  // Distinct per path: keeps the compiler from merging the two paths' loads into
+  // one block fed by copies of the offsets (a copy overwritten while its load is
+  // in flight makes the compiler wait for that load).
+  asm volatile("; chunk loads, path %0" ::"n"(PATH));
+}
+
 template <class E>
 __device__ __forceinline__ void gather(RegSet<E>& rs, const KeySource& ks, int j, const char* kbase,
                                        const char* vbase, const ThreadOffsets<E>& to) {
-  uint32_t off[E::kKIters];
-  size_t base;
   if (j < ks.n_dense) {
-    const int t0 = ks.dense_base + j * kChunk;
     rs.flag = 0;
     rs.ky0 = 0;
     rs.kx0 = 0;
-    base = (size_t)t0 * E::kRowBytes;
-    if (t0 + kChunk <= ks.dense_limit) {
-      for (int r = 0; r < E::kKIters; ++r) off[r] = to.dense[r];
-    } else {
-      // positions past the range load its last key; the tail mask drops them
-      for (int r = 0; r < E::kKIters; ++r) {
-        const int t = min(t0 + kpos_of(r, E::kPPR), ks.dense_limit - 1) - t0;
-        off[r] = (uint32_t)(t * E::kRowBytes + kcol_of(r, E::kPPR) * 16);
-      }
-    }
+    load_chunk<0>(rs, ks, kbase, vbase, ks.dense_base + j * kChunk, to.dense);
   } else {
-    const int e = j - ks.n_dense;
+    const int e = ks.e0 + j - ks.n_dense;
     const uint32_t kt = ks.key_tiles[e];
-    rs.flag = ks.flags[e];
+    rs.flag = (ks.flags32[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
     const int kty = (int)(((uint64_t)kt * ks.nkx_magic) >> 32);
     rs.ky0 = kty * kKeyH;
     rs.kx0 = ((int)kt - kty * ks.nkx) * kKeyW;
-    base = (size_t)(ks.n_text + rs.ky0 * ks.gw + rs.kx0) * E::kRowBytes;
-    if (rs.ky0 + kKeyH <= ks.gh && rs.kx0 + kKeyW <= ks.gw) {
-      for (int r = 0; r < E::kKIters; ++r) off[r] = to.tile[r];
-    } else {
-      // cells past the grid edge load an in-grid key; the mask drops them
-      for (int r = 0; r < E::kKIters; ++r) {
-        const int p = kpos_of(r, E::kPPR);
-        const int a = min(rs.ky0 + (p >> 3), ks.gh - 1) - rs.ky0;
-        const int c = min(rs.kx0 + (p & 7), ks.gw - 1) - rs.kx0;
-        off[r] = (uint32_t)((a * ks.gw + c) * E::kRowBytes + kcol_of(r, E::kPPR) * 16);
-      }
-    }
-  }
-  const char* kb = kbase + base;
-  const char* vb = vbase + base;
-  for (int r = 0; r < E::kKIters; ++r) {
-    rs.k[r] = *(const u32x4_t*)(kb + off[r]);
-    rs.v[r] = *(const u32x4_t*)(vb + off[r]);
+    load_chunk<1>(rs, ks, kbase, vbase, ks.n_text + rs.ky0 * ks.gw + rs.kx0, to.tile);
   }
 }
 
 template <class E>
-__device__ __forceinline__ void lstore(char* st, const RegSet<E>& rs) {
+__device__ __forceinline__ void lstore(char* st, uint32_t lds_k, uint32_t lds_v, const RegSet<E>& rs) {
+  static_assert(kThreads % E::kPPR == 0, "each pass covers whole rows");
+  constexpr int kRowsPerPass = kThreads / E::kPPR;
   for (int r = 0; r < E::kKIters; ++r) {
-    const int pos = kpos_of(r, E::kPPR), col = kcol_of(r, E::kPPR);
-    *(u32x4_t*)(st + E::kKOff + pos * E::kRowK + col * 16) = rs.k[r];
-    *(u32x4_t*)(st + E::kVOff + pos * E::kRowV + col * 16) = rs.v[r];
+    *(u32x4_t*)(st + lds_k + r * kRowsPerPass * E::kRowK) = rs.k[r];
+    *(u32x4_t*)(st + lds_v + r * kRowsPerPass * E::kRowV) = rs.v[r];
   }
 }
 
@@ -381,16 +397,19 @@ __device__ __forceinline__ ChunkInfo chunk_info(const RegSet<E>& rs, int j, cons
   return c;
 }
 
+enum MaskMode { kMaskNone = 0, kMaskTail = 1, kMaskCoord = 2 };
+
 // Mask, online softmax and P.V for the logits s of one chunk (one wavefront).
-template <class E>
-__device__ __forceinline__ void softmax_pv(E& eng, SoftmaxState& sm, const char* st, f32x16_t s,
+// One straight-line instance per mask mode, so the logits are masked in place.
+template <int MODE, class E>
+__device__ __forceinline__ void softmax_pv(E& eng, SoftmaxState& sm, const char* st, f32x16_t& s,
                                            const ChunkInfo& c, const KeySource& ks, int lane,
                                            int qy, int qx, int r2, float scale_log2) {
   const int g = lane >> 5;
-  if (c.tail < 32) {
+  if (MODE == 3 ? c.tail < 32 : MODE == kMaskTail) {
     for (int i = 0; i < 16; ++i)
       if (acc_row(i, g) >= c.tail) s[i] = -__builtin_inff();
-  } else if (c.coord) {
+  } else if (MODE == 3 ? c.coord : MODE == kMaskCoord) {
     // Register i of lane group g holds key cell (ky0 + i/4, kx0 + 4g + i%4) of
     // the key tile; admitted iff dx^2 <= r2 - dy^2 with both cells on the grid.
     int lim[4], dxx[4];
@@ -428,6 +447,13 @@ __device__ __forceinline__ void softmax_pv(E& eng, SoftmaxState& sm, const char*
 }
 
 template <class E>
+__device__ __forceinline__ void run_softmax_pv(E& eng, SoftmaxState& sm, const char* st, f32x16_t& s,
+                                               const ChunkInfo& c, const KeySource& ks, int lane,
+                                               int qy, int qx, int r2, float scale_log2) {
+  softmax_pv<3>(eng, sm, st, s, c, ks, lane, qy, qx, r2, scale_log2);
+}
+
+template <class E>
 __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char smem[kStages * E::kStage];
   const int tid = threadIdx.x;
@@ -448,8 +474,10 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
   ks.gw = p.gw;
   ks.nkx = p.nkx;
   ks.nkx_magic = p.nkx_magic;
-  ks.key_tiles = p.tm_key_tiles;
-  ks.flags = p.tm_flags;
+  ks.key_tiles = (const_u32_t*)p.tm_key_tiles;
+  ks.flags32 = (const_u32_t*)p.tm_flags;
+  ks.e0 = 0;
+  ks.n_tok = p.N;
   int n_chunks;
   int split = 0, tq = 0;
   if (text_wg) {
@@ -485,16 +513,18 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
     ks.dense_base = 0;
     ks.dense_limit = p.n_text;
     ks.n_dense = (p.n_text + kChunk - 1) / kChunk;
-    const uint32_t e0 = p.tm_offsets[tile];
-    ks.key_tiles = p.tm_key_tiles + e0;
-    ks.flags = p.tm_flags + e0;
-    n_chunks = ks.n_dense + (int)(p.tm_offsets[tile + 1] - e0);
+    const const_u32_t* offs = (const const_u32_t*)p.tm_offsets;
+    const uint32_t e0 = offs[tile];
+    ks.e0 = (int)e0;
+    n_chunks = ks.n_dense + (int)(offs[tile + 1] - e0);
   }
 
   const size_t head_off = (size_t)bh * p.N * E::kRowBytes;
   const char* kbase = p.k + head_off;
   const char* vbase = p.v + head_off;
 
+  const uint32_t lds_k = E::kKOff + kpos_of(0, E::kPPR) * E::kRowK + kcol_of(0, E::kPPR) * 16;
+  const uint32_t lds_v = E::kVOff + kpos_of(0, E::kPPR) * E::kRowV + kcol_of(0, E::kPPR) * 16;
   ThreadOffsets<E> toff;
   for (int r = 0; r < E::kKIters; ++r) {
     const int pp = kpos_of(r, E::kPPR), col = kcol_of(r, E::kPPR);
@@ -521,38 +551,42 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
   char* st1 = smem + E::kStage;
   char* st2 = smem + 2 * E::kStage;
   ChunkInfo ca{false, false, true, 32, 0, 0}, cb{false, false, true, 32, 0, 0};
-  if (n > 0) gather(ra, ks, 0, kbase, vbase, toff);
-  if (n > 1) gather(rb, ks, 1, kbase, vbase, toff);
+  // Every iteration issues the same loads (past the end it refetches the last
+  // chunk, which is then not used), so the compiler's load counting stays exact
+  // and each wait covers only the chunk about to be stored.
   if (n > 0) {
-    lstore(st0, ra);
+    gather(ra, ks, 0, kbase, vbase, toff);
+    gather(rb, ks, n > 1 ? 1 : 0, kbase, vbase, toff);
+    eng.settle_q();
+    lstore(st0, lds_k, lds_v, ra);
     ca = chunk_info(ra, 0, ks, wave);
+    gather(ra, ks, n > 2 ? 2 : n - 1, kbase, vbase, toff);
+    __syncthreads();
+    if (wave_active && ca.active) eng.qk(st0, lane, sa);
   }
-  if (n > 2) gather(ra, ks, 2, kbase, vbase, toff);
-  __syncthreads();
-  if (n > 0 && wave_active && ca.active) eng.qk(st0, lane, sa);
   for (int j = 0; j < n; j += 2) {
     // chunk j in (sa, ca, st0); chunk j + 1 goes to (sb, cb, st1)
     if (j + 1 < n) {
-      lstore(st1, rb);
+      lstore(st1, lds_k, lds_v, rb);
       cb = chunk_info(rb, j + 1, ks, wave);
     }
-    if (j + 3 < n) gather(rb, ks, j + 3, kbase, vbase, toff);
+    gather(rb, ks, j + 3 < n ? j + 3 : n - 1, kbase, vbase, toff);
     __syncthreads();
     if (wave_active) {
       if (j + 1 < n && cb.active) eng.qk(st1, lane, sb);
-      if (ca.active) softmax_pv(eng, sm, st0, sa, ca, ks, lane, qy, qx, p.r2, p.scale_log2);
+      if (ca.active) run_softmax_pv(eng, sm, st0, sa, ca, ks, lane, qy, qx, p.r2, p.scale_log2);
     }
     if (j + 1 >= n) break;
     // chunk j + 1 in (sb, cb, st1); chunk j + 2 goes to (sa, ca, st2)
     if (j + 2 < n) {
-      lstore(st2, ra);
+      lstore(st2, lds_k, lds_v, ra);
       ca = chunk_info(ra, j + 2, ks, wave);
     }
-    if (j + 4 < n) gather(ra, ks, j + 4, kbase, vbase, toff);
+    gather(ra, ks, j + 4 < n ? j + 4 : n - 1, kbase, vbase, toff);
     __syncthreads();
     if (wave_active) {
       if (j + 2 < n && ca.active) eng.qk(st2, lane, sa);
-      if (cb.active) softmax_pv(eng, sm, st1, sb, cb, ks, lane, qy, qx, p.r2, p.scale_log2);
+      if (cb.active) run_softmax_pv(eng, sm, st1, sb, cb, ks, lane, qy, qx, p.r2, p.scale_log2);
     }
     // stages of chunks j + 2, j + 3, j + 4
     char* t = st0;

@@ -60,7 +60,7 @@ constexpr int kTileH = CLEAR_TILE_H;
 constexpr int kTileW = CLEAR_TILE_W;
 constexpr int kSubH = CLEAR_SUB_H;
 constexpr int kChunk = CLEAR_CHUNK;
-constexpr int kStages = 3;
+constexpr int kStages = 2;
 constexpr int kKeyH = CLEAR_KEY_H;
 constexpr int kKeyW = CLEAR_KEY_W;
 constexpr int kTextQ = kWaves * 32;  // text queries per workgroup
@@ -115,16 +115,20 @@ struct Bf16 {
   static constexpr int kElem = 2;
   static constexpr int kRowBytes = D * 2;       // global row
   static constexpr int kPPR = D / 8;            // 16-byte pieces per row
-  static constexpr int kRowK = D * 2 + 16;
-  static constexpr int kRowV = D * 2 + 64;
-  static constexpr int kKOff = 0;
-  static constexpr int kVOff = kChunk * kRowK;
-  static constexpr int kStage = kVOff + kChunk * kRowV;
-  static constexpr int kKIters = kChunk * kPPR / kThreads;
+  static constexpr int kSlotsK = kPPR + 1;      // LDS row pitch in 16-byte slots (K)
+  static constexpr int kSlotsV = kPPR + 4;      // (V: transpose reads need a wider pad)
   static constexpr int kKK = D / 16;
   static constexpr int kNB = D / 32;
-  static constexpr int kWavesPerSimd = 2;   // two workgroups per CU
-  static_assert(kChunk * kPPR % kThreads == 0, "pieces must split evenly");
+  static constexpr int kWavesPerSimd = 3;
+
+  static constexpr int kRowK = kSlotsK * 16;
+  static constexpr int kRowV = kSlotsV * 16;
+  // 1 KB direct-to-LDS blocks per region, a multiple of the wavefront count
+  static constexpr int kBlocksK = (kChunk * kSlotsK + 64 * kWaves - 1) / (64 * kWaves) * kWaves;
+  static constexpr int kBlocksV = (kChunk * kSlotsV + 64 * kWaves - 1) / (64 * kWaves) * kWaves;
+  static constexpr int kKOff = 0;
+  static constexpr int kVOff = kBlocksK * 1024;
+  static constexpr int kStage = kVOff + kBlocksV * 1024;
 
   bf16x8_t q[kKK];
   f32x16_t o[kNB];
@@ -151,6 +155,8 @@ struct Bf16 {
     for (int kk = 0; kk < kKK; ++kk) {
       bf16x8_t a = *(const bf16x8_t*)(kb + kk * 32);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q[kk], s, 0, 0, 0);
+      // at most four operands in flight (register budget of three waves per SIMD)
+      if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
     }
   }
   // Probabilities as the B operand of P.V (bf16, registers 8t .. 8t+7 in
@@ -192,6 +198,7 @@ struct Bf16 {
             (lds_s16x4_t*)(lds_char_t*)const_cast<char*>(a0 + 8 * kRowV));
         s16x8_t w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pr.b[t], o[nb], 0, 0, 0);
+        if (nb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -211,16 +218,19 @@ struct F32 {
   static constexpr int kElem = 4;
   static constexpr int kRowBytes = D * 4;
   static constexpr int kPPR = D / 4;
-  static constexpr int kRowK = D * 4 + 16;
-  static constexpr int kRowV = D * 4 + 16;
-  static constexpr int kKOff = 0;
-  static constexpr int kVOff = kChunk * kRowK;
-  static constexpr int kStage = kVOff + kChunk * kRowV;
-  static constexpr int kKIters = kChunk * kPPR / kThreads;
+  static constexpr int kSlotsK = kPPR + 1;
+  static constexpr int kSlotsV = kPPR + 1;
   static constexpr int kHalf = D / 2;   // d values per lane group in Q.K
   static constexpr int kNB = D / 32;
   static constexpr int kWavesPerSimd = 1;
-  static_assert(kChunk * kPPR % kThreads == 0, "pieces must split evenly");
+
+  static constexpr int kRowK = kSlotsK * 16;
+  static constexpr int kRowV = kSlotsV * 16;
+  static constexpr int kBlocksK = (kChunk * kSlotsK + 64 * kWaves - 1) / (64 * kWaves) * kWaves;
+  static constexpr int kBlocksV = (kChunk * kSlotsV + 64 * kWaves - 1) / (64 * kWaves) * kWaves;
+  static constexpr int kKOff = 0;
+  static constexpr int kVOff = kBlocksK * 1024;
+  static constexpr int kStage = kVOff + kBlocksV * 1024;
 
   float q[kHalf];
   f32x16_t o[kNB];
@@ -288,83 +298,112 @@ struct KeySource {
   const_u32_t* flags32;    // u16 flags, two per word
 };
 
-// Byte offsets (from the chunk's first key) of the 16-byte pieces this thread
-// moves: inside a key tile that lies on the grid, and inside a dense range.
-template <class E>
-struct ThreadOffsets {
-  uint32_t tile[E::kKIters];
-  uint32_t dense[E::kKIters];
-};
-
-__device__ __forceinline__ int kpos_of(int r, int ppr) { return (threadIdx.x + r * kThreads) / ppr; }
-__device__ __forceinline__ int kcol_of(int r, int ppr) { return (threadIdx.x + r * kThreads) % ppr; }
-
-// One chunk in flight in registers: K and V pieces of this thread, and the
-// chunk's flags and key-tile origin (uniform).
-template <class E>
-struct RegSet {
-  u32x4_t k[E::kKIters];
-  u32x4_t v[E::kKIters];
-  unsigned flag;
-  int ky0, kx0;
-};
-
 // Buffer resource over `bytes` bytes from a uniform address (gfx9 resource
 // word 3).  Loads at offsets >= bytes return zero instead of touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_rsrc(const char* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Fetch chunk j into registers.  The chunk's first key row is uniform, so the
-// buffer resources carry it in scalar registers and every thread adds one of
-// two loop-invariant piece offsets (dense range, or key tile).  Pieces that fall
-// outside the chunk's keys need no special path: past the end of the head the
-// resource bound returns zeros; past the grid's right edge they read the next
-// row's keys; past a dense range's limit, the following tokens.  All of these
-// are finite and removed by the mask.
-template <int PATH, class E>
-__device__ __forceinline__ void load_chunk(RegSet<E>& rs, const KeySource& ks, const char* kbase,
-                                           const char* vbase, int tok0, const uint32_t* off) {
-  const size_t base = (size_t)tok0 * E::kRowBytes;
-  const size_t left = (size_t)(ks.n_tok - tok0) * E::kRowBytes;
-  const uint32_t bytes = left < 0x7fffffffu ? (uint32_t)left : 0x7fffffffu;
-  const __amdgpu_buffer_rsrc_t rk = byte_rsrc(kbase + base, bytes), rv = byte_rsrc(vbase + base, bytes);
-  for (int r = 0; r < E::kKIters; ++r) {
-    rs.k[r] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)off[r], 0, 0));
-    rs.v[r] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)off[r], 0, 0));
-  }
-  // Distinct per path: keeps the compiler from merging the two paths' loads into
-  // one block fed by copies of the offsets (a copy overwritten while its load is
-  // in flight makes the compiler wait for that load).
-  asm volatile("; chunk loads, path %0" ::"n"(PATH));
-}
+// Per-chunk description, uniform: where the chunk's keys start, and what the
+// mask needs.
+struct ChunkMeta {
+  int tok0;       // first key token of the chunk
+  unsigned flag;  // tile-map flags (0 for dense chunks)
+  int ky0, kx0;   // key-tile origin (image chunks)
+};
 
-template <class E>
-__device__ __forceinline__ void gather(RegSet<E>& rs, const KeySource& ks, int j, const char* kbase,
-                                       const char* vbase, const ThreadOffsets<E>& to) {
+__device__ __forceinline__ ChunkMeta chunk_meta(const KeySource& ks, int j) {
+  ChunkMeta m;
   if (j < ks.n_dense) {
-    rs.flag = 0;
-    rs.ky0 = 0;
-    rs.kx0 = 0;
-    load_chunk<0>(rs, ks, kbase, vbase, ks.dense_base + j * kChunk, to.dense);
+    m.tok0 = ks.dense_base + j * kChunk;
+    m.flag = 0;
+    m.ky0 = 0;
+    m.kx0 = 0;
   } else {
     const int e = ks.e0 + j - ks.n_dense;
     const uint32_t kt = ks.key_tiles[e];
-    rs.flag = (ks.flags32[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+    m.flag = (ks.flags32[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
     const int kty = (int)(((uint64_t)kt * ks.nkx_magic) >> 32);
-    rs.ky0 = kty * kKeyH;
-    rs.kx0 = ((int)kt - kty * ks.nkx) * kKeyW;
-    load_chunk<1>(rs, ks, kbase, vbase, ks.n_text + rs.ky0 * ks.gw + rs.kx0, to.tile);
+    m.ky0 = kty * kKeyH;
+    m.kx0 = ((int)kt - kty * ks.nkx) * kKeyW;
+    m.tok0 = ks.n_text + m.ky0 * ks.gw + m.kx0;
+  }
+  return m;
+}
+
+// Staging a chunk into LDS with direct-to-LDS buffer loads.  One load
+// instruction of a wavefront fills one 1 KB block (lane l writes 16-byte slot
+// 64 * block + l); the K region holds key rows at a pitch of kSlotsK slots, the
+// V region at kSlotsV, so a slot is either piece p of row r or row padding.
+// Block b of a region goes to wavefront b % 4 (regions are padded to a
+// multiple of four blocks, so every wavefront issues the same loads).  Each lane keeps, per block it
+// fills, the byte offset of its piece from the chunk's first key: one for a
+// dense token range and one for a key tile (rows 8 apart on the grid).
+// Padding slots get an offset past any buffer bound and load zeros.
+template <class E>
+struct DmaPlan {
+  static constexpr int kPerWaveK = E::kBlocksK / kWaves;
+  static constexpr int kPerWaveV = E::kBlocksV / kWaves;
+  uint32_t dense_k[kPerWaveK], tile_k[kPerWaveK];
+  uint32_t dense_v[kPerWaveV], tile_v[kPerWaveV];
+};
+
+constexpr uint32_t kNoPiece = 0xfffffff0u;
+
+template <class E>
+__device__ __forceinline__ void slot_offsets(int slot, int slots_per_row, int gw, uint32_t& dense,
+                                             uint32_t& tile) {
+  const int r = slot / slots_per_row, pc = slot - r * slots_per_row;
+  if (r >= kChunk || pc >= E::kPPR) {
+    dense = tile = kNoPiece;
+  } else {
+    dense = (uint32_t)(r * E::kRowBytes + pc * 16);
+    tile = (uint32_t)((((r >> 3) * gw) + (r & 7)) * E::kRowBytes + pc * 16);
   }
 }
 
 template <class E>
-__device__ __forceinline__ void lstore(char* st, uint32_t lds_k, uint32_t lds_v, const RegSet<E>& rs) {
-  static_assert(kThreads % E::kPPR == 0, "each pass covers whole rows");
-  constexpr int kRowsPerPass = kThreads / E::kPPR;
-  for (int r = 0; r < E::kKIters; ++r) {
-    *(u32x4_t*)(st + lds_k + r * kRowsPerPass * E::kRowK) = rs.k[r];
-    *(u32x4_t*)(st + lds_v + r * kRowsPerPass * E::kRowV) = rs.v[r];
+__device__ __forceinline__ DmaPlan<E> make_plan(int wave, int lane, int gw) {
+  DmaPlan<E> pl;
+  for (int i = 0; i < DmaPlan<E>::kPerWaveK; ++i)
+    slot_offsets<E>(64 * (wave + kWaves * i) + lane, E::kSlotsK, gw, pl.dense_k[i], pl.tile_k[i]);
+  for (int i = 0; i < DmaPlan<E>::kPerWaveV; ++i)
+    slot_offsets<E>(64 * (wave + kWaves * i) + lane, E::kSlotsV, gw, pl.dense_v[i], pl.tile_v[i]);
+  return pl;
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <class E>
+__device__ __forceinline__ void dma_blocks(char* st, int wave, __amdgpu_buffer_rsrc_t rk,
+                                           __amdgpu_buffer_rsrc_t rv, const uint32_t* ok,
+                                           const uint32_t* ov) {
+  char* sk = st + E::kKOff + 1024 * wave;
+  char* sv = st + E::kVOff + 1024 * wave;
+  for (int i = 0; i < DmaPlan<E>::kPerWaveK; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(sk + 1024 * kWaves * i), 16, (int)ok[i], 0, 0, 0);
+  for (int i = 0; i < DmaPlan<E>::kPerWaveV; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(sv + 1024 * kWaves * i), 16, (int)ov[i], 0, 0, 0);
+}
+
+// Start the copy of a chunk into LDS stage st.  The buffer resources start at
+// the chunk's first key and end with the head, so pieces past the head read
+// zeros; pieces past the grid's right edge read the next row's keys, pieces
+// past a dense range's limit the following tokens: all finite and masked.
+template <class E>
+__device__ __forceinline__ void stage_chunk(char* st, const ChunkMeta& m, bool dense, int wave,
+                                            const KeySource& ks, const char* kbase, const char* vbase,
+                                            const DmaPlan<E>& pl) {
+  const size_t base = (size_t)m.tok0 * E::kRowBytes;
+  const size_t left = (size_t)(ks.n_tok - m.tok0) * E::kRowBytes;
+  const uint32_t bytes = left < 0x7fffffffu ? (uint32_t)left : 0x7fffffffu;
+  const __amdgpu_buffer_rsrc_t rk = byte_rsrc(kbase + base, bytes), rv = byte_rsrc(vbase + base, bytes);
+  if (dense) {
+    dma_blocks<E>(st, wave, rk, rv, pl.dense_k, pl.dense_v);
+    asm volatile("; stage dense chunk");
+  } else {
+    dma_blocks<E>(st, wave, rk, rv, pl.tile_k, pl.tile_v);
+    asm volatile("; stage key tile");
   }
 }
 
@@ -382,17 +421,15 @@ struct ChunkInfo {
   int ky0, kx0;
 };
 
-template <class E>
-__device__ __forceinline__ ChunkInfo chunk_info(const RegSet<E>& rs, int j, const KeySource& ks,
-                                                int wave) {
-  ChunkInfo c{true, false, true, 32, rs.ky0, rs.kx0};
+__device__ __forceinline__ ChunkInfo chunk_info(const ChunkMeta& m, int j, const KeySource& ks, int wave) {
+  ChunkInfo c{true, false, true, 32, m.ky0, m.kx0};
   if (j < ks.n_dense) {
-    const int rem = ks.dense_limit - (ks.dense_base + j * kChunk);
+    const int rem = ks.dense_limit - m.tok0;
     c.tail = rem < 32 ? rem : 32;
   } else {
-    c.active = (rs.flag >> wave) & 1u;
-    c.coord = !((rs.flag >> (8 + wave)) & 1u);
-    c.inside = rs.ky0 + kKeyH <= ks.gh && rs.kx0 + kKeyW <= ks.gw;
+    c.active = (m.flag >> wave) & 1u;
+    c.coord = !((m.flag >> (8 + wave)) & 1u);
+    c.inside = m.ky0 + kKeyH <= ks.gh && m.kx0 + kKeyW <= ks.gw;
   }
   return c;
 }
@@ -523,76 +560,45 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
   const char* kbase = p.k + head_off;
   const char* vbase = p.v + head_off;
 
-  const uint32_t lds_k = E::kKOff + kpos_of(0, E::kPPR) * E::kRowK + kcol_of(0, E::kPPR) * 16;
-  const uint32_t lds_v = E::kVOff + kpos_of(0, E::kPPR) * E::kRowV + kcol_of(0, E::kPPR) * 16;
-  ThreadOffsets<E> toff;
-  for (int r = 0; r < E::kKIters; ++r) {
-    const int pp = kpos_of(r, E::kPPR), col = kcol_of(r, E::kPPR);
-    toff.tile[r] = (uint32_t)((((pp >> 3) * p.gw) + (pp & 7)) * E::kRowBytes + col * 16);
-    toff.dense[r] = (uint32_t)(pp * E::kRowBytes + col * 16);
-  }
+  const DmaPlan<E> plan = make_plan<E>(wave, lane, p.gw);
 
   E eng;
   eng.load_q(p.q + head_off + (size_t)(qvalid ? qtok : 0) * E::kRowBytes, qvalid, g);
   eng.zero_o();
-  const bool wave_active = __ballot(qvalid) != 0ull;
   SoftmaxState sm{kMInit, 0.0f};
 
-  // ---- pipelined main loop.  Chunk c is fetched into registers at iteration
-  // c - 2, written to LDS stage c % 3 at iteration c - 1 and consumed at
-  // iteration c.  After the barrier of iteration j, chunks j and j + 1 are both
-  // in LDS: the wavefront issues the Q.K products of chunk j + 1 before the
-  // softmax and P.V of chunk j, so matrix-core work overlaps the softmax.
-  RegSet<E> ra, rb;  // chunks in flight: even chunks in ra, odd chunks in rb
-  f32x16_t sa, sb;   // logits of the current / next chunk (alternating)
+  // ---- chunk loop.  Two LDS stages: after the barrier of iteration j, chunk
+  // j is in stage j % 2 (its direct-to-LDS loads were issued in iteration
+  // j - 1 and are complete: the barrier waits for each wavefront's loads), and
+  // every wavefront is done with chunk j - 1, so the loads of chunk j + 1 can
+  // go to the other stage while chunk j is computed.  The scalar description of
+  // chunk j + 2 is fetched before the barrier, where the wait is paid anyway.
   const int n = n_chunks;
-  // LDS stages of chunks j, j + 1, j + 2 (rotated every two iterations)
-  char* st0 = smem;
-  char* st1 = smem + E::kStage;
-  char* st2 = smem + 2 * E::kStage;
-  ChunkInfo ca{false, false, true, 32, 0, 0}, cb{false, false, true, 32, 0, 0};
-  // Every iteration issues the same loads (past the end it refetches the last
-  // chunk, which is then not used), so the compiler's load counting stays exact
-  // and each wait covers only the chunk about to be stored.
+  char* st_cur = smem;
+  char* st_nxt = smem + E::kStage;
+  eng.settle_q();
   if (n > 0) {
-    gather(ra, ks, 0, kbase, vbase, toff);
-    gather(rb, ks, n > 1 ? 1 : 0, kbase, vbase, toff);
-    eng.settle_q();
-    lstore(st0, lds_k, lds_v, ra);
-    ca = chunk_info(ra, 0, ks, wave);
-    gather(ra, ks, n > 2 ? 2 : n - 1, kbase, vbase, toff);
-    __syncthreads();
-    if (wave_active && ca.active) eng.qk(st0, lane, sa);
-  }
-  for (int j = 0; j < n; j += 2) {
-    // chunk j in (sa, ca, st0); chunk j + 1 goes to (sb, cb, st1)
-    if (j + 1 < n) {
-      lstore(st1, lds_k, lds_v, rb);
-      cb = chunk_info(rb, j + 1, ks, wave);
+    ChunkMeta m_cur = chunk_meta(ks, 0);
+    ChunkMeta m_nxt = chunk_meta(ks, n > 1 ? 1 : 0);
+    stage_chunk<E>(st_cur, m_cur, 0 < ks.n_dense, wave, ks, kbase, vbase, plan);
+    for (int j = 0; j < n; ++j) {
+      __syncthreads();
+      if (j + 1 < n) stage_chunk<E>(st_nxt, m_nxt, j + 1 < ks.n_dense, wave, ks, kbase, vbase, plan);
+      const ChunkInfo c = chunk_info(m_cur, j, ks, wave);
+      // Every wavefront computes every chunk: one that its sub-tile does not
+      // touch is fully masked (zero probabilities, O unchanged).  Skipping it
+      // would put O on two paths and cost a copy of O per chunk.
+      {
+        f32x16_t sc;
+        eng.qk(st_cur, lane, sc);
+        run_softmax_pv(eng, sm, st_cur, sc, c, ks, lane, qy, qx, p.r2, p.scale_log2);
+      }
+      m_cur = m_nxt;
+      m_nxt = chunk_meta(ks, j + 2 < n ? j + 2 : n - 1);
+      char* t = st_cur;
+      st_cur = st_nxt;
+      st_nxt = t;
     }
-    gather(rb, ks, j + 3 < n ? j + 3 : n - 1, kbase, vbase, toff);
-    __syncthreads();
-    if (wave_active) {
-      if (j + 1 < n && cb.active) eng.qk(st1, lane, sb);
-      if (ca.active) run_softmax_pv(eng, sm, st0, sa, ca, ks, lane, qy, qx, p.r2, p.scale_log2);
-    }
-    if (j + 1 >= n) break;
-    // chunk j + 1 in (sb, cb, st1); chunk j + 2 goes to (sa, ca, st2)
-    if (j + 2 < n) {
-      lstore(st2, lds_k, lds_v, ra);
-      ca = chunk_info(ra, j + 2, ks, wave);
-    }
-    gather(ra, ks, j + 4 < n ? j + 4 : n - 1, kbase, vbase, toff);
-    __syncthreads();
-    if (wave_active) {
-      if (j + 2 < n && ca.active) eng.qk(st2, lane, sa);
-      if (cb.active) run_softmax_pv(eng, sm, st1, sb, cb, ks, lane, qy, qx, p.r2, p.scale_log2);
-    }
-    // stages of chunks j + 2, j + 3, j + 4
-    char* t = st0;
-    st0 = st2;
-    st2 = st1;
-    st1 = t;
   }
 
   // ---- epilogue

@@ -144,6 +144,10 @@ struct Bf16 {
   __device__ void zero_o() {
     for (int nb = 0; nb < kNB; ++nb) o[nb] = f32x16_t{};
   }
+  __device__ void scale_o(float a) {
+    for (int nb = 0; nb < kNB; ++nb)
+      for (int i = 0; i < 16; ++i) o[nb][i] *= a;
+  }
   // Waits for the Q loads here, once, so that no wait for them is left
   // inside the chunk loop (where it would also wait for the prefetches).
   __device__ void settle_q() {
@@ -163,6 +167,7 @@ struct Bf16 {
   // operand t) and their sum, taken over the rounded values P.V uses.
   struct Probs {
     bf16x8_t b[2];
+    __device__ void zero() { b[0] = b[1] = bf16x8_t{}; }
   };
   __device__ static float probs(const f32x16_t& e, Probs& pr) {
     const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -244,6 +249,10 @@ struct F32 {
   __device__ void zero_o() {
     for (int nb = 0; nb < kNB; ++nb) o[nb] = f32x16_t{};
   }
+  __device__ void scale_o(float a) {
+    for (int nb = 0; nb < kNB; ++nb)
+      for (int i = 0; i < 16; ++i) o[nb][i] *= a;
+  }
   __device__ void settle_q() {
     for (int i = 0; i < kHalf; ++i) asm volatile("" ::"v"(q[i]));
   }
@@ -258,6 +267,7 @@ struct F32 {
   }
   struct Probs {
     f32x16_t p;
+    __device__ void zero() { p = f32x16_t{}; }
   };
   __device__ static float probs(const f32x16_t& e, Probs& pr) {
     float l = 0.0f;
@@ -438,15 +448,18 @@ enum MaskMode { kMaskNone = 0, kMaskTail = 1, kMaskCoord = 2 };
 
 // Mask, online softmax and P.V for the logits s of one chunk (one wavefront).
 // One straight-line instance per mask mode, so the logits are masked in place.
-template <int MODE, class E>
-__device__ __forceinline__ void softmax_pv(E& eng, SoftmaxState& sm, const char* st, f32x16_t& s,
-                                           const ChunkInfo& c, const KeySource& ks, int lane,
-                                           int qy, int qx, int r2, float scale_log2) {
+// Logits of one chunk -> masked, online-softmax probabilities (base 2, lazy
+// reference max).  Returns the factor O must be scaled by before this chunk's
+// P.V (1 unless the reference max moved); O itself is not touched here, so the
+// caller can skip this step for a chunk the wavefront does not touch.
+template <class E>
+__device__ __forceinline__ float chunk_probs(SoftmaxState& sm, f32x16_t& s, const ChunkInfo& c,
+                                             const KeySource& ks, int lane, int qy, int qx, int r2,
+                                             float scale_log2, typename E::Probs& pr) {
   const int g = lane >> 5;
-  if (MODE == 3 ? c.tail < 32 : MODE == kMaskTail) {
-    for (int i = 0; i < 16; ++i)
-      if (acc_row(i, g) >= c.tail) s[i] = -__builtin_inff();
-  } else if (MODE == 3 ? c.coord : MODE == kMaskCoord) {
+  if (c.tail < 32) {
+    for (int i = 0; i < 16; ++i) s[i] = acc_row(i, g) >= c.tail ? -__builtin_inff() : s[i];
+  } else if (c.coord) {
     // Register i of lane group g holds key cell (ky0 + i/4, kx0 + 4g + i%4) of
     // the key tile; admitted iff dx^2 <= r2 - dy^2 with both cells on the grid.
     int lim[4], dxx[4];
@@ -459,35 +472,22 @@ __device__ __forceinline__ void softmax_pv(E& eng, SoftmaxState& sm, const char*
       for (int b = 0; b < 4; ++b)
         if (c.kx0 + 4 * g + b >= ks.gw) dxx[b] = 0x7fffffff;
     }
-    for (int i = 0; i < 16; ++i)
-      if (dxx[i & 3] > lim[i >> 2]) s[i] = -__builtin_inff();
+    for (int i = 0; i < 16; ++i) s[i] = dxx[i & 3] > lim[i >> 2] ? -__builtin_inff() : s[i];
   }
-
-  // online softmax (base 2, lazy reference max)
   float mx = s[0];
   for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
   mx = max_xor32(mx);
   const float mxs = mx * scale_log2;
+  float alpha = 1.0f;
   if (__ballot(mxs > sm.M + kLazyTau) != 0ull) {
     const float Mn = fmaxf(sm.M, mxs);
-    const float alpha = __builtin_amdgcn_exp2f(sm.M - Mn);
+    alpha = __builtin_amdgcn_exp2f(sm.M - Mn);
     sm.L *= alpha;
-    for (int nb = 0; nb < E::kNB; ++nb)
-      for (int i = 0; i < 16; ++i) eng.o[nb][i] *= alpha;
     sm.M = Mn;
   }
-  f32x16_t e;
-  for (int i = 0; i < 16; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -sm.M));
-  typename E::Probs pr;
-  sm.L += E::probs(e, pr);
-  eng.pv(st, lane, pr);
-}
-
-template <class E>
-__device__ __forceinline__ void run_softmax_pv(E& eng, SoftmaxState& sm, const char* st, f32x16_t& s,
-                                               const ChunkInfo& c, const KeySource& ks, int lane,
-                                               int qy, int qx, int r2, float scale_log2) {
-  softmax_pv<3>(eng, sm, st, s, c, ks, lane, qy, qx, r2, scale_log2);
+  for (int i = 0; i < 16; ++i) s[i] = __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -sm.M));
+  sm.L += E::probs(s, pr);
+  return alpha;
 }
 
 template <class E>
@@ -585,14 +585,20 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
       __syncthreads();
       if (j + 1 < n) stage_chunk<E>(st_nxt, m_nxt, j + 1 < ks.n_dense, wave, ks, kbase, vbase, plan);
       const ChunkInfo c = chunk_info(m_cur, j, ks, wave);
-      // Every wavefront computes every chunk: one that its sub-tile does not
-      // touch is fully masked (zero probabilities, O unchanged).  Skipping it
-      // would put O on two paths and cost a copy of O per chunk.
-      {
+      // A chunk the wavefront's sub-tile does not touch skips Q.K and the
+      // softmax: its probabilities are zero.  P.V and the rescale of O stay
+      // outside the branch, so O is updated on one path only.
+      typename E::Probs pr;
+      float alpha = 1.0f;
+      if (c.active) {
         f32x16_t sc;
         eng.qk(st_cur, lane, sc);
-        run_softmax_pv(eng, sm, st_cur, sc, c, ks, lane, qy, qx, p.r2, p.scale_log2);
+        alpha = chunk_probs<E>(sm, sc, c, ks, lane, qy, qx, p.r2, p.scale_log2, pr);
+      } else {
+        pr.zero();
       }
+      if (__ballot(alpha != 1.0f) != 0ull) eng.scale_o(alpha);
+      eng.pv(st_cur, lane, pr);
       m_cur = m_nxt;
       m_nxt = chunk_meta(ks, j + 2 < n ? j + 2 : n - 1);
       char* t = st_cur;

@@ -56,20 +56,27 @@ def admitted_pairs(n_text: int, gh: int, gw: int, r2: int) -> int:
     return img + gh * gw * n_text + n_text * n
 
 
-def computed_pairs(ca, n_text: int, gh: int, gw: int, r2: int) -> int:
-    """Pairs the kernels actually evaluate (tile waste included), from the tile map."""
+def computed_pairs(ca, n_text: int, gh: int, gw: int, r2: int) -> float:
+    """Query-key products the kernels evaluate per head, tile waste included, in
+    pair units (one pair = Q.K plus P.V work, 4d flops).  Per 32-query x 32-key
+    chunk of a wavefront: Q.K runs for text chunks and for listed key tiles its
+    sub-tile touches; P.V runs for every chunk (untouched ones with zero
+    probabilities).  Text workgroups run every chunk of all N keys."""
     import numpy as np
 
     tm = ca.tile_map_build(gh, gw, r2)
     f = tm["flags"].astype(np.int64)
-    per_wave_img = sum(int(((f >> w) & 1).sum()) for w in range(4)) * ca.KEY_H * ca.KEY_W * 32
-    ntx = -(-gw // ca.TILE_W)
-    nty = -(-gh // ca.TILE_H)
-    waves_on = sum(min(4, max(0, -(-(gh - ty * 16) // 4))) for ty in range(nty)) * ntx
-    text_keys = -(-n_text // ca.CHUNK) * ca.CHUNK
+    nsub = (ca.TILE_H // ca.SUB_H) * (ca.TILE_W // ca.SUB_W)
+    touched = sum(int(((f >> w) & 1).sum()) for w in range(nsub))
+    ntiles = (-(-gh // ca.TILE_H)) * (-(-gw // ca.TILE_W))
+    per_chunk = ca.CHUNK * 32
+    text_chunks = -(-n_text // ca.CHUNK)
+    dense = ntiles * nsub * text_chunks
+    qk = dense + touched
+    pv = dense + len(f) * nsub
     n = n_text + gh * gw
-    text_rows = -(-n_text // 128) * 128 * (-(-n // ca.CHUNK) * ca.CHUNK)
-    return per_wave_img + waves_on * 32 * text_keys + text_rows
+    text_rows = -(-n_text // 128) * 4 * (-(-n // ca.CHUNK))
+    return (0.5 * (qk + pv) + text_rows) * per_chunk
 
 
 def kernel_source_hash() -> str:

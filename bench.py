@@ -37,13 +37,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def admitted_pairs(n_text: int, gh: int, gw: int, r2: int) -> int:
+def admitted_pairs(n_text: int, gh: int, gw: int, r2: int, window: str = "circle") -> int:
     """Admitted (query, key) pairs of one head: for each window offset (dy, dx)
     with dy^2 + dx^2 <= r2, (gh - |dy|)(gw - |dx|) image queries have that key on
     the grid; image queries also admit the n_text text keys; text queries admit
-    all N keys."""
+    all N keys.  The square window (max(dy^2, dx^2) <= r2) factors into one sum
+    per axis."""
     img = 0
-    if r2 >= 0:
+    if r2 >= 0 and window == "square":
+        w = math.isqrt(r2)
+        img = (sum(gh - abs(d) for d in range(-w, w + 1) if abs(d) < gh)
+               * sum(gw - abs(d) for d in range(-w, w + 1) if abs(d) < gw))
+    elif r2 >= 0:
         w = math.isqrt(r2)
         for dy in range(-w, w + 1):
             if abs(dy) >= gh:
@@ -56,7 +61,7 @@ def admitted_pairs(n_text: int, gh: int, gw: int, r2: int) -> int:
     return img + gh * gw * n_text + n_text * n
 
 
-def computed_pairs(ca, n_text: int, gh: int, gw: int, r2: int) -> float:
+def computed_pairs(ca, n_text: int, gh: int, gw: int, r2: int, window: str = "circle") -> float:
     """Query-key products the kernels evaluate per head, tile waste included, in
     pair units (one pair = Q.K plus P.V work, 4d flops).  Per 32-query x 32-key
     chunk of a wavefront: Q.K runs for text chunks and for listed key tiles its
@@ -64,7 +69,7 @@ def computed_pairs(ca, n_text: int, gh: int, gw: int, r2: int) -> float:
     probabilities).  Text workgroups run every chunk of all N keys."""
     import numpy as np
 
-    tm = ca.tile_map_build(gh, gw, r2)
+    tm = ca.tile_map_build(gh, gw, r2, window=window)
     f = tm["flags"].astype(np.int64)
     nsub = (ca.TILE_H // ca.SUB_H) * (ca.TILE_W // ca.SUB_W)
     touched = sum(int(((f >> w) & 1).sum()) for w in range(nsub))
@@ -102,15 +107,16 @@ def load_traffic(workload: str, radius: int):
     return e.get("hbm_bytes_per_launch")
 
 
-def time_layer(ca, torch, q, k, v, w, radius, steps, warmup):
+def time_layer(ca, torch, q, k, v, w, radius, steps, warmup, window="circle"):
     out = torch.empty_like(q)
+    kw = {} if window == "circle" else {"window": window}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ca.fwd(q, k, v, w.n_text, w.grid_h, w.grid_w, radius=radius, out=out)   # builds the tile map
+    ca.fwd(q, k, v, w.n_text, w.grid_h, w.grid_w, radius=radius, out=out, **kw)   # builds the tile map
     torch.cuda.synchronize()
     first_ms = (time.perf_counter() - t0) * 1e3
     for _ in range(warmup):
-        ca.fwd(q, k, v, w.n_text, w.grid_h, w.grid_w, radius=radius, out=out)
+        ca.fwd(q, k, v, w.n_text, w.grid_h, w.grid_w, radius=radius, out=out, **kw)
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
@@ -118,7 +124,7 @@ def time_layer(ca, torch, q, k, v, w, radius, steps, warmup):
     t0 = time.perf_counter()
     for s, e in ev:
         s.record(stream)
-        ca.fwd(q, k, v, w.n_text, w.grid_h, w.grid_w, radius=radius, out=out)
+        ca.fwd(q, k, v, w.n_text, w.grid_h, w.grid_w, radius=radius, out=out, **kw)
         e.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
@@ -183,6 +189,8 @@ def main():
     ap.add_argument("--workload", default="flux8k")
     ap.add_argument("--radius", type=int, default=32)
     ap.add_argument("--also-radius", type=int, default=8, help="second radius timed alongside (-1: none)")
+    ap.add_argument("--square-radius", type=int, default=32,
+                    help="also time the square-window variant at this radius (-1: none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -235,6 +243,23 @@ def main():
         log(f"r={r}: {t['ms_per_step']:.3f} ms/layer, {t['in_window_tflops']:.1f} TFLOP/s in-window "
             f"({t['pct_bf16_peak']:.1f}% of bf16 peak), kernel {t['kernel_ms_mean']:.3f} ms")
 
+    square = None
+    if args.square_radius >= 0:
+        r = args.square_radius
+        t, _ = time_layer(ca, torch, q, k, v, w, r, args.steps, args.warmup, window="square")
+        pairs = admitted_pairs(w.n_text, w.grid_h, w.grid_w, r * r, "square")
+        flops = 4.0 * w.d * pairs * w.B * w.H
+        cpairs = computed_pairs(ca, w.n_text, w.grid_h, w.grid_w, r * r, "square")
+        square = {
+            "radius": r,
+            "ms_per_layer": round(t["ms_per_step"], 4),
+            "in_window_tflops": round(flops / (t["ms_per_step"] * 1e-3) / 1e12, 3),
+            "pct_bf16_peak": round(100.0 * flops / (t["ms_per_step"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "computed_tflops": round(4.0 * w.d * cpairs * w.B * w.H / (t["ms_per_step"] * 1e-3) / 1e12, 3),
+            "admitted_pairs_per_head": pairs,
+        }
+        log(f"square window r={r}: {t['ms_per_step']:.3f} ms/layer, {square['in_window_tflops']:.1f} TFLOP/s in-window")
+
     main_r = args.radius
     m = results[main_r]
     achieved = m["flops_per_layer"] / (m["kernel_ms_mean"] * 1e-3) / 1e12
@@ -281,6 +306,8 @@ def main():
             "pct_bf16_peak": round(t["pct_bf16_peak"], 2),
             "computed_tflops": round(t["computed_tflops"], 3),
         }
+    if square is not None:
+        line[f"square_r{square['radius']}"] = square
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on a sample (~{args.cpu_seconds:.0f} s)...")
         line["cpu_baseline"] = cpu_baseline(q, k, v, w, main_r, args.cpu_seconds)

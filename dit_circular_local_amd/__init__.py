@@ -21,7 +21,7 @@ __all__ = [
     "ClearError", "fwd", "tile_map_size", "tile_map_build", "tile_map_build_device",
     "release_cache", "last_error", "version", "lib", "EXPORTS",
     "CLEAR_OK", "CLEAR_EINVAL", "CLEAR_ENOMEM", "CLEAR_EHIP", "CLEAR_ENOTSUP",
-    "CLEAR_BF16", "CLEAR_FP32", "TILE_H", "TILE_W", "SUB_H", "SUB_W", "KEY_H", "KEY_W", "CHUNK",
+    "CLEAR_BF16", "CLEAR_FP32", "CLEAR_WINDOW_CIRCLE", "CLEAR_WINDOW_SQUARE", "WINDOWS", "TILE_H", "TILE_W", "SUB_H", "SUB_W", "KEY_H", "KEY_W", "CHUNK",
     "MAX_GRID",
 ]
 
@@ -29,13 +29,16 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libclear_at
 
 CLEAR_OK, CLEAR_EINVAL, CLEAR_ENOMEM, CLEAR_EHIP, CLEAR_ENOTSUP = 0, -22, -12, -5, -95
 CLEAR_BF16, CLEAR_FP32 = 0, 1
+CLEAR_WINDOW_CIRCLE, CLEAR_WINDOW_SQUARE = 0, 1
+WINDOWS = {"circle": CLEAR_WINDOW_CIRCLE, "square": CLEAR_WINDOW_SQUARE}
 TILE_H, TILE_W, SUB_H, SUB_W, KEY_H, KEY_W, CHUNK = 16, 8, 4, 8, 4, 8, 32
 MAX_GRID = 8192
 
 # every entry point declared in include/clear_attn.h
 EXPORTS = (
     "clear_attn_fwd", "clear_attn_fwd_ex", "clear_tile_map_size", "clear_tile_map_build",
-    "clear_tile_map_build_device", "clear_last_error", "clear_release_cache", "clear_version",
+    "clear_tile_map_build_device", "clear_tile_map_size_ex", "clear_tile_map_build_ex",
+    "clear_tile_map_build_device_ex", "clear_last_error", "clear_release_cache", "clear_version",
 )
 
 
@@ -47,7 +50,7 @@ class ClearError(RuntimeError):
 
 class _Opts(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int), ("r2_max", ctypes.c_int),
-                ("lse_out", ctypes.c_void_p), ("text_splits", ctypes.c_int)]
+                ("lse_out", ctypes.c_void_p), ("text_splits", ctypes.c_int), ("window", ctypes.c_int)]
 
 
 _lib = None
@@ -73,6 +76,12 @@ def lib():
     L.clear_tile_map_build.restype = i
     L.clear_tile_map_build_device.argtypes = [i, i, i, i, i, i, i, i, i, p, p, p, sz, szp, p]
     L.clear_tile_map_build_device.restype = i
+    L.clear_tile_map_size_ex.argtypes = [i] + L.clear_tile_map_size.argtypes
+    L.clear_tile_map_size_ex.restype = i
+    L.clear_tile_map_build_ex.argtypes = [i] + L.clear_tile_map_build.argtypes
+    L.clear_tile_map_build_ex.restype = i
+    L.clear_tile_map_build_device_ex.argtypes = [i] + L.clear_tile_map_build_device.argtypes
+    L.clear_tile_map_build_device_ex.restype = i
     L.clear_last_error.argtypes = []
     L.clear_last_error.restype = ctypes.c_char_p
     L.clear_release_cache.argtypes = []
@@ -105,13 +114,20 @@ def _stream_of(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+def _window_code(window: str) -> int:
+    if window not in WINDOWS:
+        raise ValueError(f"window must be one of {sorted(WINDOWS)} (got {window!r})")
+    return WINDOWS[window]
+
+
 def fwd(q, k, v, n_text: int, grid_h: int, grid_w: int, radius: Optional[int] = None,
         r2: Optional[int] = None, out=None, return_lse: bool = False, text_splits: int = 0,
-        use_ex: Optional[bool] = None):
+        use_ex: Optional[bool] = None, window: str = "circle"):
     """CLEAR attention forward on torch tensors [B, H, N, d] (bf16 or fp32, on the GPU).
 
     Give either ``radius`` (r2 = radius^2, the "<=" reading) or ``r2`` directly
     (e.g. radius^2 - 1 for the strict "<" reading, -1 for no image keys).
+    ``window="square"`` selects the square-window variant (max(dy^2, dx^2) <= r2).
     Returns ``out`` or ``(out, lse)``.
     """
     import torch
@@ -142,8 +158,12 @@ def fwd(q, k, v, n_text: int, grid_h: int, grid_w: int, radius: Optional[int] = 
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
     stream = _stream_of(q)
     L = lib()
+    wcode = _window_code(window)
     if use_ex is None:
-        use_ex = not (dtype == CLEAR_BF16 and r2 is None and not return_lse and text_splits == 0)
+        use_ex = not (dtype == CLEAR_BF16 and r2 is None and not return_lse and text_splits == 0
+                      and wcode == CLEAR_WINDOW_CIRCLE)
+    if not use_ex and wcode != CLEAR_WINDOW_CIRCLE:
+        raise ValueError("the square window needs the _ex entry point")
     if not use_ex:
         rc = L.clear_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                               B, H, d, n_text, grid_h, grid_w, int(radius), stream)
@@ -152,7 +172,7 @@ def fwd(q, k, v, n_text: int, grid_h: int, grid_w: int, radius: Optional[int] = 
             if radius < 0:
                 raise ValueError("radius must be >= 0")
             r2 = min(int(radius) * int(radius), 2 ** 31 - 1)
-        opts = _Opts(dtype, int(r2), lse.data_ptr() if lse is not None else None, int(text_splits))
+        opts = _Opts(dtype, int(r2), lse.data_ptr() if lse is not None else None, int(text_splits), wcode)
         rc = L.clear_attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                  B, H, d, n_text, grid_h, grid_w, ctypes.byref(opts), stream)
     _check(rc)
@@ -160,10 +180,10 @@ def fwd(q, k, v, n_text: int, grid_h: int, grid_w: int, radius: Optional[int] = 
 
 
 def tile_map_size(grid_h, grid_w, r2, tile_h=TILE_H, tile_w=TILE_W, sub_h=SUB_H, sub_w=SUB_W,
-                  key_h=KEY_H, key_w=KEY_W):
+                  key_h=KEY_H, key_w=KEY_W, window: str = "circle"):
     n = ctypes.c_size_t()
-    _check(lib().clear_tile_map_size(grid_h, grid_w, r2, tile_h, tile_w, sub_h, sub_w, key_h, key_w,
-                                     ctypes.byref(n)))
+    _check(lib().clear_tile_map_size_ex(_window_code(window), grid_h, grid_w, r2, tile_h, tile_w, sub_h,
+                                        sub_w, key_h, key_w, ctypes.byref(n)))
     return n.value
 
 
@@ -172,36 +192,36 @@ def _ntiles(grid_h, grid_w, tile_h, tile_w):
 
 
 def tile_map_build(grid_h, grid_w, r2, tile_h=TILE_H, tile_w=TILE_W, sub_h=SUB_H, sub_w=SUB_W,
-                   key_h=KEY_H, key_w=KEY_W):
+                   key_h=KEY_H, key_w=KEY_W, window: str = "circle"):
     """Host-built tile map as numpy arrays (layout in include/clear_attn.h)."""
     L = lib()
-    n = tile_map_size(grid_h, grid_w, r2, tile_h, tile_w, sub_h, sub_w, key_h, key_w)
+    n = tile_map_size(grid_h, grid_w, r2, tile_h, tile_w, sub_h, sub_w, key_h, key_w, window)
     nt = _ntiles(grid_h, grid_w, tile_h, tile_w)
     off = np.zeros(nt + 1, np.uint32)
     kt = np.zeros(max(n, 1), np.uint32)
     fl = np.zeros(max(n, 1), np.uint16)
     got = ctypes.c_size_t()
-    _check(L.clear_tile_map_build(grid_h, grid_w, r2, tile_h, tile_w, sub_h, sub_w, key_h, key_w,
-                                  off.ctypes.data, kt.ctypes.data, fl.ctypes.data, n,
-                                  ctypes.byref(got)))
+    _check(L.clear_tile_map_build_ex(_window_code(window), grid_h, grid_w, r2, tile_h, tile_w, sub_h,
+                                     sub_w, key_h, key_w, off.ctypes.data, kt.ctypes.data,
+                                     fl.ctypes.data, n, ctypes.byref(got)))
     return {"offsets": off, "key_tiles": kt[:n], "flags": fl[:n]}
 
 
 def tile_map_build_device(grid_h, grid_w, r2, tile_h=TILE_H, tile_w=TILE_W, sub_h=SUB_H,
-                          sub_w=SUB_W, key_h=KEY_H, key_w=KEY_W, device="cuda"):
+                          sub_w=SUB_W, key_h=KEY_H, key_w=KEY_W, device="cuda", window: str = "circle"):
     """Device-built tile map; returns numpy copies of the device arrays."""
     import torch
 
     L = lib()
-    n = tile_map_size(grid_h, grid_w, r2, tile_h, tile_w, sub_h, sub_w, key_h, key_w)
+    n = tile_map_size(grid_h, grid_w, r2, tile_h, tile_w, sub_h, sub_w, key_h, key_w, window)
     nt = _ntiles(grid_h, grid_w, tile_h, tile_w)
     off = torch.zeros(nt + 1, dtype=torch.int32, device=device)
     kt = torch.zeros(max(n, 1), dtype=torch.int32, device=device)
     fl = torch.zeros(max(n, 1), dtype=torch.int16, device=device)
     got = ctypes.c_size_t()
-    _check(L.clear_tile_map_build_device(grid_h, grid_w, r2, tile_h, tile_w, sub_h, sub_w, key_h,
-                                         key_w, off.data_ptr(), kt.data_ptr(), fl.data_ptr(), n,
-                                         ctypes.byref(got), _stream_of(off)))
+    _check(L.clear_tile_map_build_device_ex(_window_code(window), grid_h, grid_w, r2, tile_h, tile_w,
+                                            sub_h, sub_w, key_h, key_w, off.data_ptr(), kt.data_ptr(),
+                                            fl.data_ptr(), n, ctypes.byref(got), _stream_of(off)))
     torch.cuda.current_stream(off.device).synchronize()
     return {
         "offsets": off.cpu().numpy().view(np.uint32),

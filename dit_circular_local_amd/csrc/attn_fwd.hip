@@ -84,7 +84,7 @@ struct Params {
   const uint32_t* tm_offsets;
   const uint32_t* tm_key_tiles;
   const uint16_t* tm_flags;
-  int N, n_text, gh, gw, r2;
+  int N, n_text, gh, gw, r2, window;
   int ntiles, ntx, nkx;
   uint64_t nkx_magic;
   int n_text_blocks, splits, chunks_per_split;
@@ -303,6 +303,7 @@ struct KeySource {
   int n_text, gh, gw, nkx;
   uint64_t nkx_magic;    // ceil(2^32 / nkx): kt / nkx == (kt * magic) >> 32 here
   int e0;                // the query tile's first tile-map entry
+  int window;            // 0 circle, 1 square
   int n_tok;             // tokens per head (N)
   const_u32_t* key_tiles;  // whole tile map, read through the scalar cache
   const_u32_t* flags32;    // u16 flags, two per word
@@ -426,13 +427,15 @@ struct SoftmaxState {
 struct ChunkInfo {
   bool active;
   bool coord;
+  bool square;  // square-window variant
   bool inside;  // key tile wholly on the grid
   int tail;     // dense chunk: positions >= tail are masked
   int ky0, kx0;
 };
 
 __device__ __forceinline__ ChunkInfo chunk_info(const ChunkMeta& m, int j, const KeySource& ks, int wave) {
-  ChunkInfo c{true, false, true, 32, m.ky0, m.kx0};
+  ChunkInfo c{true, false, false, true, 32, m.ky0, m.kx0};
+  c.square = ks.window == 1;
   if (j < ks.n_dense) {
     const int rem = ks.dense_limit - m.tok0;
     c.tail = rem < 32 ? rem : 32;
@@ -461,10 +464,15 @@ __device__ __forceinline__ float chunk_probs(SoftmaxState& sm, f32x16_t& s, cons
     for (int i = 0; i < 16; ++i) s[i] = acc_row(i, g) >= c.tail ? -__builtin_inff() : s[i];
   } else if (c.coord) {
     // Register i of lane group g holds key cell (ky0 + i/4, kx0 + 4g + i%4) of
-    // the key tile; admitted iff dx^2 <= r2 - dy^2 with both cells on the grid.
+    // the key tile; admitted iff dx^2 <= lim, lim = r2 - dy^2 (circle) or
+    // lim = dy^2 <= r2 ? r2 : -1 (square), with both cells on the grid.
     int lim[4], dxx[4];
     const int dy0 = qy - c.ky0, dx0 = qx - c.kx0 - 4 * g;
-    for (int a = 0; a < 4; ++a) lim[a] = r2 - __mul24(dy0 - a, dy0 - a);
+    if (c.square) {
+      for (int a = 0; a < 4; ++a) lim[a] = __mul24(dy0 - a, dy0 - a) <= r2 ? r2 : -1;
+    } else {
+      for (int a = 0; a < 4; ++a) lim[a] = r2 - __mul24(dy0 - a, dy0 - a);
+    }
     for (int b = 0; b < 4; ++b) dxx[b] = __mul24(dx0 - b, dx0 - b);
     if (!c.inside) {
       for (int a = 0; a < 4; ++a)
@@ -515,6 +523,7 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
   ks.flags32 = (const_u32_t*)p.tm_flags;
   ks.e0 = 0;
   ks.n_tok = p.N;
+  ks.window = p.window;
   int n_chunks;
   int split = 0, tq = 0;
   if (text_wg) {
@@ -691,6 +700,7 @@ int attn_launch(const AttnLaunch& a, void* stream) {
   p.gh = a.gh;
   p.gw = a.gw;
   p.r2 = a.r2;
+  p.window = a.window;
   p.ntx = (a.gw + kTileW - 1) / kTileW;
   p.ntiles = ((a.gh + kTileH - 1) / kTileH) * p.ntx;
   p.nkx = (a.gw + kKeyW - 1) / kKeyW;

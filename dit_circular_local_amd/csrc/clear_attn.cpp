@@ -27,7 +27,7 @@ struct TileMapDev {
 };
 
 struct DevState {
-  std::map<std::tuple<int, int, int>, TileMapDev> maps;
+  std::map<std::tuple<int, int, int, int>, TileMapDev> maps;  // (gh, gw, r2, window)
   void* ws = nullptr;
   size_t ws_bytes = 0;
 };
@@ -41,12 +41,13 @@ int hip_fail(hipError_t e, const char* what) {
   return set_error(CLEAR_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Tile map of the kernels' fixed tiling for (gh, gw, r2) on the current device;
-// built on `stream` on first use.  Caller holds g_mu.
-int get_tile_map(DevState& ds, int gh, int gw, int r2, hipStream_t stream, TileMapDev** out) {
+// Tile map of the kernels' fixed tiling for (gh, gw, r2, window) on the current
+// device; built on `stream` on first use.  Caller holds g_mu.
+int get_tile_map(DevState& ds, int gh, int gw, int r2, int window, hipStream_t stream,
+                 TileMapDev** out) {
   TileGeom g = make_geom(gh, gw, r2, CLEAR_TILE_H, CLEAR_TILE_W, CLEAR_SUB_H, CLEAR_SUB_W, CLEAR_KEY_H,
-                         CLEAR_KEY_W);
-  auto key = std::make_tuple(gh, gw, g.r2);
+                         CLEAR_KEY_W, window);
+  auto key = std::make_tuple(gh, gw, g.r2, window);
   auto it = ds.maps.find(key);
   if (it != ds.maps.end()) {
     *out = &it->second;
@@ -91,7 +92,7 @@ int choose_text_splits(int B, int H, int n_text, int N, int ntiles, size_t img_c
   // wavefront-chunks of work (each = 32 queries x 32 keys)
   const double w_img = (double)B * H * (4.0 * ntiles * nt_ch + 3.0 * (double)img_chunks);
   const double w_text = (double)B * H * text_blocks * 4.0 * nall;
-  const double slots = 256.0 * 4.0 * 2.0;  // CUs x SIMDs x resident waves
+  const double slots = 256.0 * 4.0 * 3.0;  // CUs x SIMDs x resident waves
   const double t_ideal = (w_img + w_text) / slots;
   int s = (int)(2.0 * nall / (t_ideal > 1.0 ? t_ideal : 1.0)) + 1;
   int smax = (int)(nall / 8.0);
@@ -133,13 +134,13 @@ using namespace clear;
 
 extern "C" const char* clear_last_error(void) { return g_err; }
 
-extern "C" int clear_version(void) { return 100; }
+extern "C" int clear_version(void) { return 10100; }
 
 extern "C" int clear_attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B,
                                  int H, int d, int n_text, int grid_h, int grid_w,
                                  const clear_opts* opts, void* stream) {
   clear_error_reset();
-  clear_opts o = opts ? *opts : clear_opts{CLEAR_BF16, 0, nullptr, 0};
+  clear_opts o = opts ? *opts : clear_opts{CLEAR_BF16, 0, nullptr, 0, CLEAR_WINDOW_CIRCLE};
   if (!q || !k || !v || !out) return set_error(CLEAR_EINVAL, "q, k, v and out must not be NULL");
   if (B < 1 || H < 1) return set_error(CLEAR_EINVAL, "B and H must be >= 1 (got %d, %d)", B, H);
   if (d != 64 && d != 128) return set_error(CLEAR_EINVAL, "d must be 64 or 128 (got %d)", d);
@@ -149,6 +150,9 @@ extern "C" int clear_attn_fwd_ex(const void* q, const void* k, const void* v, vo
   if (o.dtype != CLEAR_BF16 && o.dtype != CLEAR_FP32)
     return set_error(CLEAR_EINVAL, "dtype must be CLEAR_BF16 or CLEAR_FP32 (got %d)", o.dtype);
   if (o.r2_max < -1) return set_error(CLEAR_EINVAL, "r2_max must be >= -1 (got %d)", o.r2_max);
+  if (o.window != CLEAR_WINDOW_CIRCLE && o.window != CLEAR_WINDOW_SQUARE)
+    return set_error(CLEAR_EINVAL, "window must be CLEAR_WINDOW_CIRCLE or CLEAR_WINDOW_SQUARE (got %d)",
+                     o.window);
   if (n_text == 0 && o.r2_max < 0)
     return set_error(CLEAR_EINVAL, "n_text == 0 and r2_max < 0: every query row would be empty");
   if (o.text_splits < 0 || o.text_splits > 64)
@@ -172,12 +176,12 @@ extern "C" int clear_attn_fwd_ex(const void* q, const void* k, const void* v, vo
   std::lock_guard<std::mutex> lock(g_mu);
   DevState& ds = g_dev[dev];
   TileMapDev* tm = nullptr;
-  int rc = get_tile_map(ds, grid_h, grid_w, o.r2_max, s, &tm);
+  int rc = get_tile_map(ds, grid_h, grid_w, o.r2_max, o.window, s, &tm);
   if (rc) return rc;
   if ((e = hipStreamWaitEvent(s, tm->ready, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
 
   TileGeom g = make_geom(grid_h, grid_w, o.r2_max, CLEAR_TILE_H, CLEAR_TILE_W, CLEAR_SUB_H, CLEAR_SUB_W,
-                         CLEAR_KEY_H, CLEAR_KEY_W);
+                         CLEAR_KEY_H, CLEAR_KEY_W, o.window);
   int splits = o.text_splits ? o.text_splits
                              : choose_text_splits(B, H, n_text, (int)N, g.nty * g.ntx, tm->n_entries);
   AttnLaunch a;
@@ -185,7 +189,7 @@ extern "C" int clear_attn_fwd_ex(const void* q, const void* k, const void* v, vo
   a.q = q; a.k = k; a.v = v; a.out = out; a.lse = o.lse_out;
   a.tm_offsets = tm->offsets; a.tm_key_tiles = tm->key_tiles; a.tm_flags = tm->flags;
   a.B = B; a.H = H; a.d = d; a.n_text = n_text; a.gh = grid_h; a.gw = grid_w; a.r2 = g.r2;
-  a.dtype = o.dtype; a.text_splits = splits;
+  a.dtype = o.dtype; a.text_splits = splits; a.window = o.window;
   if (splits > 1 && n_text > 0) {
     const size_t o_bytes = align_up((size_t)splits * B * H * n_text * d * 4, 256);
     const size_t need = o_bytes + (size_t)splits * B * H * n_text * 2 * 4;
@@ -219,19 +223,23 @@ extern "C" int clear_attn_fwd(const void* q, const void* k, const void* v, void*
   if (radius < 0) return set_error(CLEAR_EINVAL, "radius must be >= 0 (got %d)", radius);
   long long r2 = (long long)radius * radius;
   if (r2 > 0x7fffffffLL) r2 = 0x7fffffffLL;
-  clear_opts o{CLEAR_BF16, (int)r2, nullptr, 0};
+  clear_opts o{CLEAR_BF16, (int)r2, nullptr, 0, CLEAR_WINDOW_CIRCLE};
   return clear_attn_fwd_ex(q, k, v, out, B, H, d, n_text, grid_h, grid_w, &o, stream);
 }
 
-extern "C" int clear_tile_map_build_device(int grid_h, int grid_w, int r2_max, int tile_h, int tile_w,
-                                           int sub_h, int sub_w, int key_h, int key_w, uint32_t* offsets,
-                                           uint32_t* key_tiles, uint16_t* flags, size_t cap,
-                                           size_t* n_entries, void* stream) {
+extern "C" int clear_tile_map_build_device_ex(int window, int grid_h, int grid_w, int r2_max,
+                                              int tile_h, int tile_w, int sub_h, int sub_w, int key_h,
+                                              int key_w, uint32_t* offsets, uint32_t* key_tiles,
+                                              uint16_t* flags, size_t cap, size_t* n_entries,
+                                              void* stream) {
   clear_error_reset();
+  if (window != CLEAR_WINDOW_CIRCLE && window != CLEAR_WINDOW_SQUARE)
+    return set_error(CLEAR_EINVAL, "window must be CLEAR_WINDOW_CIRCLE or CLEAR_WINDOW_SQUARE (got %d)",
+                     window);
   int rc = tile_map_validate(grid_h, grid_w, r2_max, tile_h, tile_w, sub_h, sub_w, key_h, key_w);
   if (rc) return rc;
   if (!n_entries) return set_error(CLEAR_EINVAL, "n_entries must not be NULL");
-  TileGeom g = make_geom(grid_h, grid_w, r2_max, tile_h, tile_w, sub_h, sub_w, key_h, key_w);
+  TileGeom g = make_geom(grid_h, grid_w, r2_max, tile_h, tile_w, sub_h, sub_w, key_h, key_w, window);
   *n_entries = tile_map_count(g);
   if (*n_entries > cap)
     return set_error(CLEAR_ENOMEM, "tile map needs %zu entries (capacity %zu)", *n_entries, cap);
@@ -244,6 +252,15 @@ extern "C" int clear_tile_map_build_device(int grid_h, int grid_w, int r2_max, i
     if (e != hipSuccess) return hip_fail(e, "CLEAR_DEBUG sync");
   }
   return CLEAR_OK;
+}
+
+extern "C" int clear_tile_map_build_device(int grid_h, int grid_w, int r2_max, int tile_h, int tile_w,
+                                           int sub_h, int sub_w, int key_h, int key_w, uint32_t* offsets,
+                                           uint32_t* key_tiles, uint16_t* flags, size_t cap,
+                                           size_t* n_entries, void* stream) {
+  return clear_tile_map_build_device_ex(CLEAR_WINDOW_CIRCLE, grid_h, grid_w, r2_max, tile_h, tile_w,
+                                        sub_h, sub_w, key_h, key_w, offsets, key_tiles, flags, cap,
+                                        n_entries, stream);
 }
 
 extern "C" void clear_release_cache(void) {

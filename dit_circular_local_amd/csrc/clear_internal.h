@@ -39,6 +39,7 @@ struct AttnLaunch {
   int B, H, d, n_text, gh, gw, r2;
   int dtype;
   int text_splits;
+  int window;                 // CLEAR_WINDOW_CIRCLE or CLEAR_WINDOW_SQUARE
 };
 
 int attn_launch(const AttnLaunch& a, void* stream);

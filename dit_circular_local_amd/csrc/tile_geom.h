@@ -1,4 +1,5 @@
-// tile_geom.h -- closed-form geometry of CLEAR's circular window over tiles.
+// tile_geom.h -- closed-form geometry of CLEAR's circular window (and of the
+// square-window variant) over tiles.
 //
 // Shared by the host and the device tile-map builders (which must agree bit for
 // bit).  The window is the image part of CLEAR's mask (pith.science review of
@@ -12,6 +13,12 @@
 // dy^2 plus that of dx^2, and those are attained at interval ends.  So a
 // sub-tile touches a key tile iff dymin^2 + dxmin^2 <= r2, and admits every pair
 // iff dymax^2 + dxmax^2 <= r2.
+//
+// Square-window variant (the square the circle is inscribed in, against which
+// the same review's "What carries the argument" prices the circle at about
+// pi/4): key cell admitted when max((qy-ky)^2, (qx-kx)^2) <= r2.  The same
+// argument gives touched iff max(dymin^2, dxmin^2) <= r2 and full iff
+// max(dymax^2, dxmax^2) <= r2.
 #pragma once
 
 #include <stdint.h>
@@ -24,8 +31,11 @@
 
 namespace clear {
 
+enum { kWindowCircle = 0, kWindowSquare = 1 };
+
 struct TileGeom {
   int gh, gw, r2;     // grid and squared radius (r2 already clamped to the grid diagonal)
+  int window;         // kWindowCircle or kWindowSquare
   int th, tw;         // query tile
   int sh, sw;         // sub-tile (one wavefront)
   int kh, kw;         // key tile
@@ -49,11 +59,12 @@ CLEAR_HD int isqrt_exact(int x) {
 }
 
 CLEAR_HD TileGeom make_geom(int gh, int gw, int r2, int th, int tw, int sh, int sw, int kh,
-                            int kw) {
+                            int kw, int window = kWindowCircle) {
   TileGeom g;
   g.gh = gh; g.gw = gw;
-  // Admitting every pair needs at most the grid diagonal; clamping keeps all
-  // squares in 32-bit range without changing the mask.
+  g.window = window;
+  // Admitting every pair needs at most the grid diagonal (either window);
+  // clamping keeps all squares in 32-bit range without changing the mask.
   int64_t diag = (int64_t)(gh - 1) * (gh - 1) + (int64_t)(gw - 1) * (gw - 1);
   g.r2 = (int64_t)r2 > diag ? (int)diag : r2;
   g.th = th; g.tw = tw; g.sh = sh; g.sw = sw; g.kh = kh; g.kw = kw;
@@ -86,6 +97,11 @@ CLEAR_HD void candidate_key_tiles(const TileGeom& g, int y0, int y1, int x0, int
   kx_hi = imin(g.gw - 1, x1 + g.wmax) / g.kw;
 }
 
+// The window predicate on squared offsets.
+CLEAR_HD bool window_admits(const TileGeom& g, int dy2, int dx2) {
+  return g.window == kWindowSquare ? imax(dy2, dx2) <= g.r2 : dy2 + dx2 <= g.r2;
+}
+
 // Min / max of |a - b| over a in [a0, a1], b in [b0, b1].
 CLEAR_HD void interval_dist(int a0, int a1, int b0, int b1, int& dmin, int& dmax) {
   dmin = imax(0, imax(b0 - a1, a0 - b1));
@@ -108,9 +124,9 @@ CLEAR_HD unsigned key_tile_flags(const TileGeom& g, int ty0, int tx0, int kty, i
     int dymin, dymax, dxmin, dxmax;
     interval_dist(sy0, sy1, ky0, ky1, dymin, dymax);
     interval_dist(sx0, sx1, kx0, kx1, dxmin, dxmax);
-    if (dymin * dymin + dxmin * dxmin <= g.r2) {
+    if (window_admits(g, dymin * dymin, dxmin * dxmin)) {
       f |= 1u << s;
-      if (on_grid && dymax * dymax + dxmax * dxmax <= g.r2) f |= 1u << (8 + s);
+      if (on_grid && window_admits(g, dymax * dymax, dxmax * dxmax)) f |= 1u << (8 + s);
     }
   }
   return f;

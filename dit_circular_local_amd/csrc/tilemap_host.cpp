@@ -71,26 +71,38 @@ void tile_map_fill_host(const TileGeom& g, uint32_t* offsets, uint32_t* key_tile
 
 using namespace clear;
 
-extern "C" int clear_tile_map_size(int grid_h, int grid_w, int r2_max, int tile_h, int tile_w,
-                                   int sub_h, int sub_w, int key_h, int key_w, size_t* n_entries) {
+static int window_validate(int window) {
+  if (window != CLEAR_WINDOW_CIRCLE && window != CLEAR_WINDOW_SQUARE)
+    return set_error(CLEAR_EINVAL, "window must be CLEAR_WINDOW_CIRCLE or CLEAR_WINDOW_SQUARE (got %d)",
+                     window);
+  return CLEAR_OK;
+}
+
+extern "C" int clear_tile_map_size_ex(int window, int grid_h, int grid_w, int r2_max, int tile_h,
+                                      int tile_w, int sub_h, int sub_w, int key_h, int key_w,
+                                      size_t* n_entries) {
   clear_error_reset();
-  int rc = tile_map_validate(grid_h, grid_w, r2_max, tile_h, tile_w, sub_h, sub_w, key_h, key_w);
+  int rc = window_validate(window);
+  if (rc) return rc;
+  rc = tile_map_validate(grid_h, grid_w, r2_max, tile_h, tile_w, sub_h, sub_w, key_h, key_w);
   if (rc) return rc;
   if (!n_entries) return set_error(CLEAR_EINVAL, "n_entries must not be NULL");
-  TileGeom g = make_geom(grid_h, grid_w, r2_max, tile_h, tile_w, sub_h, sub_w, key_h, key_w);
+  TileGeom g = make_geom(grid_h, grid_w, r2_max, tile_h, tile_w, sub_h, sub_w, key_h, key_w, window);
   *n_entries = tile_map_count(g);
   return CLEAR_OK;
 }
 
-extern "C" int clear_tile_map_build(int grid_h, int grid_w, int r2_max, int tile_h, int tile_w,
-                                    int sub_h, int sub_w, int key_h, int key_w, uint32_t* offsets,
-                                    uint32_t* key_tiles, uint16_t* flags, size_t cap,
-                                    size_t* n_entries) {
+extern "C" int clear_tile_map_build_ex(int window, int grid_h, int grid_w, int r2_max, int tile_h,
+                                       int tile_w, int sub_h, int sub_w, int key_h, int key_w,
+                                       uint32_t* offsets, uint32_t* key_tiles, uint16_t* flags,
+                                       size_t cap, size_t* n_entries) {
   clear_error_reset();
-  int rc = tile_map_validate(grid_h, grid_w, r2_max, tile_h, tile_w, sub_h, sub_w, key_h, key_w);
+  int rc = window_validate(window);
+  if (rc) return rc;
+  rc = tile_map_validate(grid_h, grid_w, r2_max, tile_h, tile_w, sub_h, sub_w, key_h, key_w);
   if (rc) return rc;
   if (!n_entries) return set_error(CLEAR_EINVAL, "n_entries must not be NULL");
-  TileGeom g = make_geom(grid_h, grid_w, r2_max, tile_h, tile_w, sub_h, sub_w, key_h, key_w);
+  TileGeom g = make_geom(grid_h, grid_w, r2_max, tile_h, tile_w, sub_h, sub_w, key_h, key_w, window);
   *n_entries = tile_map_count(g);
   if (*n_entries > cap)
     return set_error(CLEAR_ENOMEM, "tile map needs %zu entries (capacity %zu)", *n_entries, cap);
@@ -98,4 +110,18 @@ extern "C" int clear_tile_map_build(int grid_h, int grid_w, int r2_max, int tile
     return set_error(CLEAR_EINVAL, "tile map output pointers must not be NULL");
   tile_map_fill_host(g, offsets, key_tiles, flags);
   return CLEAR_OK;
+}
+
+extern "C" int clear_tile_map_size(int grid_h, int grid_w, int r2_max, int tile_h, int tile_w,
+                                   int sub_h, int sub_w, int key_h, int key_w, size_t* n_entries) {
+  return clear_tile_map_size_ex(CLEAR_WINDOW_CIRCLE, grid_h, grid_w, r2_max, tile_h, tile_w, sub_h,
+                                sub_w, key_h, key_w, n_entries);
+}
+
+extern "C" int clear_tile_map_build(int grid_h, int grid_w, int r2_max, int tile_h, int tile_w,
+                                    int sub_h, int sub_w, int key_h, int key_w, uint32_t* offsets,
+                                    uint32_t* key_tiles, uint16_t* flags, size_t cap,
+                                    size_t* n_entries) {
+  return clear_tile_map_build_ex(CLEAR_WINDOW_CIRCLE, grid_h, grid_w, r2_max, tile_h, tile_w, sub_h,
+                                 sub_w, key_h, key_w, offsets, key_tiles, flags, cap, n_entries);
 }

@@ -19,6 +19,11 @@
  * "< r^2", which on the integer lattice is r2 = radius^2 - 1 (pass it through
  * clear_attn_fwd_ex).  A negative r2 admits no image key.
  *
+ * Square-window variant (CLEAR_WINDOW_SQUARE; not CLEAR's mask: the square the
+ * circle is inscribed in, against which the review's "What carries the
+ * argument" prices the circle at about pi/4): the image condition becomes
+ * max(dy^2, dx^2) <= r2, i.e. max(|dy|, |dx|) <= isqrt(r2).
+ *
  * Conventions shared by every entry point
  *   - Return value: CLEAR_OK (0) or a negative error code below.  On error
  *     nothing has been launched or written, and clear_last_error() describes
@@ -52,6 +57,9 @@ extern "C" {
 #define CLEAR_BF16 0
 #define CLEAR_FP32 1
 
+#define CLEAR_WINDOW_CIRCLE 0  /* dy^2 + dx^2 <= r2 (CLEAR)      */
+#define CLEAR_WINDOW_SQUARE 1  /* max(dy^2, dx^2) <= r2 (variant) */
+
 /* Tiling of the attention kernels: a workgroup owns a 16 x 8 cell query tile;
  * each of its four wavefronts owns a 4 x 8 sub-tile; image keys stream in 4 x 8
  * cell key tiles (32 keys), text keys in chunks of 32.  clear_tile_map_build*
@@ -74,6 +82,8 @@ typedef struct clear_opts {
                        log-sum-exp of each row's admitted logits; NULL = skip  */
   int text_splits;  /* text rows: number of key-range splits merged exactly by
                        log-sum-exp; 0 = chosen by the library; 1..64          */
+  int window;       /* CLEAR_WINDOW_CIRCLE (0) or CLEAR_WINDOW_SQUARE (1)
+                       (added in version 1.1; zero-initialise the struct)     */
 } clear_opts;
 
 /*
@@ -101,8 +111,9 @@ int clear_attn_fwd(const void* q, const void* k, const void* v, void* out,
  * clear_attn_fwd_ex -- as clear_attn_fwd with options: element type (bf16 or
  * fp32; fp32 runs fp32 matrix-core products and keeps probabilities in fp32),
  * explicit r2_max (-1 .. any; n_text == 0 with r2_max < 0 leaves every row
- * empty and returns CLEAR_EINVAL), optional LSE output and the text-row split
- * count.  opts == NULL means {CLEAR_BF16, 0, NULL, 0}.
+ * empty and returns CLEAR_EINVAL), optional LSE output, the text-row split
+ * count and the window.  opts == NULL means {CLEAR_BF16, 0, NULL, 0,
+ * CLEAR_WINDOW_CIRCLE}.
  */
 int clear_attn_fwd_ex(const void* q, const void* k, const void* v, void* out,
                       int B, int H, int d, int n_text, int grid_h, int grid_w,
@@ -154,6 +165,27 @@ int clear_tile_map_build_device(int grid_h, int grid_w, int r2_max, int tile_h,
                                 int tile_w, int sub_h, int sub_w, int key_h, int key_w,
                                 uint32_t* offsets, uint32_t* key_tiles, uint16_t* flags,
                                 size_t cap, size_t* n_entries, void* stream);
+
+/*
+ * clear_tile_map_size_ex / clear_tile_map_build_ex / clear_tile_map_build_device_ex
+ * -- the same three operations for either window (first argument
+ * CLEAR_WINDOW_CIRCLE or CLEAR_WINDOW_SQUARE; any other value returns
+ * CLEAR_EINVAL).  The functions without _ex build the circular window.  For the
+ * square window a sub-tile touches a key tile iff some pair has
+ * max(dy^2, dx^2) <= r2_max, and admits it fully iff every pair does.
+ */
+int clear_tile_map_size_ex(int window, int grid_h, int grid_w, int r2_max, int tile_h,
+                           int tile_w, int sub_h, int sub_w, int key_h, int key_w,
+                           size_t* n_entries);
+int clear_tile_map_build_ex(int window, int grid_h, int grid_w, int r2_max, int tile_h,
+                            int tile_w, int sub_h, int sub_w, int key_h, int key_w,
+                            uint32_t* offsets, uint32_t* key_tiles, uint16_t* flags,
+                            size_t cap, size_t* n_entries);
+int clear_tile_map_build_device_ex(int window, int grid_h, int grid_w, int r2_max,
+                                   int tile_h, int tile_w, int sub_h, int sub_w, int key_h,
+                                   int key_w, uint32_t* offsets, uint32_t* key_tiles,
+                                   uint16_t* flags, size_t cap, size_t* n_entries,
+                                   void* stream);
 
 /* Message of the last error raised on the calling thread ("" if none). */
 const char* clear_last_error(void);

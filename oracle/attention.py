@@ -18,6 +18,14 @@ the strict "<" the review prints is ``r2 = r*r - 1`` on the integer lattice.
 A negative ``r2`` admits no image key at all.  Keys outside the grid do not
 exist (no padding, no wrap-around).
 
+Square window (a variant, not CLEAR's own mask)
+-----------------------------------------------
+The same review ("What carries the argument") weighs the circular window
+against the square window it is inscribed in (the circle costs about pi/4 of
+it).  ``window="square"`` replaces the distance test by
+max(dy^2, dx^2) <= r2, i.e. max(|dy|, |dx|) <= isqrt(r2): the square of half
+side r for r2 = r*r.  Everything else is unchanged.
+
 Attention
 ---------
 s_ij = (q_i . k_j) / sqrt(d)            (Eq. 1 / Eq. 7 of the paper, as quoted
@@ -37,6 +45,7 @@ from typing import Iterable, Optional, Sequence
 import numpy as np
 
 __all__ = [
+    "WINDOWS",
     "clear_mask",
     "attention_rows",
     "attention_head",
@@ -55,14 +64,22 @@ def _coords(idx: np.ndarray, n_text: int, grid_w: int):
     return p // grid_w, p % grid_w
 
 
+WINDOWS = ("circle", "square")
+
+
 def clear_mask(rows: Sequence[int], cols: Sequence[int], n_text: int,
-               grid_w: int, r2: int) -> np.ndarray:
+               grid_w: int, r2: int, window: str = "circle") -> np.ndarray:
     """Boolean mask M[rows, cols], evaluated element by element from its definition."""
     i = np.asarray(rows, dtype=np.int64)[:, None]
     j = np.asarray(cols, dtype=np.int64)[None, :]
     yi, xi = _coords(i, n_text, grid_w)
     yj, xj = _coords(j, n_text, grid_w)
-    near = (yi - yj) ** 2 + (xi - xj) ** 2 <= r2
+    if window == "circle":
+        near = (yi - yj) ** 2 + (xi - xj) ** 2 <= r2
+    elif window == "square":
+        near = np.maximum((yi - yj) ** 2, (xi - xj) ** 2) <= r2
+    else:
+        raise ValueError(f"unknown window {window!r}")
     return (i < n_text) | (j < n_text) | near
 
 
@@ -93,7 +110,7 @@ def _check(n_text: int, grid_h: int, grid_w: int, r2: int, n: int):
 
 def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_text: int,
                    grid_h: int, grid_w: int, r2: int, rows: Iterable[int],
-                   return_probs: bool = False):
+                   return_probs: bool = False, window: str = "circle"):
     """Exact output rows of one (batch, head) slice, each over all N keys.
 
     q, k, v: [N, d] arrays (any float dtype, widened to float64).
@@ -107,7 +124,7 @@ def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_text: int,
     n, d = k.shape
     _check(n_text, grid_h, grid_w, r2, n)
     rows = np.asarray(list(rows), dtype=np.int64)
-    mask = clear_mask(rows, np.arange(n), n_text, grid_w, r2)
+    mask = clear_mask(rows, np.arange(n), n_text, grid_w, r2, window)
     out, lse, p = _masked_softmax_attention(q[rows], k, v, mask, 1.0 / math.sqrt(d))
     if return_probs:
         return out, lse, p
@@ -119,8 +136,8 @@ def _image_block_candidates(y0: int, y1: int, x0: int, x1: int, n_text: int,
     """Text keys plus the image keys of the clipped box [y0-w, y1+w] x [x0-w, x1+w].
 
     w = isqrt(r2): a key outside that box has |dy| > w or |dx| > w, so
-    dy^2 + dx^2 > r2 and the mask rejects it.  The box only saves work; the
-    mask is still evaluated on every candidate.
+    dy^2 + dx^2 > r2 and max(dy^2, dx^2) > r2: either window rejects it.  The
+    box only saves work; the mask is still evaluated on every candidate.
     """
     text = np.arange(n_text, dtype=np.int64)
     if r2 < 0:
@@ -135,7 +152,7 @@ def _image_block_candidates(y0: int, y1: int, x0: int, x1: int, n_text: int,
 def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_text: int,
                    grid_h: int, grid_w: int, r2: int, block: int = 8,
                    text_rows: Optional[Sequence[int]] = None,
-                   blocks: Optional[Sequence[tuple]] = None):
+                   blocks: Optional[Sequence[tuple]] = None, window: str = "circle"):
     """CLEAR attention for one (batch, head) slice.
 
     q, k, v: [N, d] arrays.  Returns (out [N, d] float64, lse [N] float64).
@@ -162,7 +179,7 @@ def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_text: int,
     all_keys = np.arange(n, dtype=np.int64)
     for s in range(0, len(trows), 64):
         rows = trows[s:s + 64]
-        mask = clear_mask(rows, all_keys, n_text, grid_w, r2)
+        mask = clear_mask(rows, all_keys, n_text, grid_w, r2, window)
         o, l_, _ = _masked_softmax_attention(q[rows], k, v, mask, scale)
         out[rows], lse[rows] = o, l_
 
@@ -177,20 +194,20 @@ def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_text: int,
         xs = np.arange(x0, x1 + 1)
         rows = n_text + (ys[:, None] * grid_w + xs[None, :]).ravel()
         cols = _image_block_candidates(y0, y1, x0, x1, n_text, grid_h, grid_w, r2)
-        mask = clear_mask(rows, cols, n_text, grid_w, r2)
+        mask = clear_mask(rows, cols, n_text, grid_w, r2, window)
         o, l_, _ = _masked_softmax_attention(q[rows], k[cols], v[cols], mask, scale)
         out[rows], lse[rows] = o, l_
     return out, lse
 
 
 def _head_job(args):
-    qh, kh, vh, n_text, grid_h, grid_w, r2, block = args
-    return attention_head(qh, kh, vh, n_text, grid_h, grid_w, r2, block)
+    qh, kh, vh, n_text, grid_h, grid_w, r2, block, window = args
+    return attention_head(qh, kh, vh, n_text, grid_h, grid_w, r2, block, window=window)
 
 
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_text: int,
               grid_h: int, grid_w: int, r2: int, block: int = 8,
-              workers: int = 1):
+              workers: int = 1, window: str = "circle"):
     """CLEAR attention for [B, H, N, d] inputs.  Returns (out, lse) in float64.
 
     Batches and heads are independent; with ``workers > 1`` they are spread
@@ -198,7 +215,7 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_text: int,
     """
     q = np.asarray(q)
     B, H, N, d = q.shape
-    jobs = [(q[b, h], k[b, h], v[b, h], n_text, grid_h, grid_w, r2, block)
+    jobs = [(q[b, h], k[b, h], v[b, h], n_text, grid_h, grid_w, r2, block, window)
             for b in range(B) for h in range(H)]
     if workers > 1 and len(jobs) > 1:
         import multiprocessing as mp
@@ -214,7 +231,8 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_text: int,
 
 def in_window_pairs(n_text: int, grid_h: int, grid_w: int, r2: int,
                     text_rows: Optional[Sequence[int]] = None,
-                    blocks: Optional[Sequence[tuple]] = None, block: int = 8) -> int:
+                    blocks: Optional[Sequence[tuple]] = None, block: int = 8,
+                    window: str = "circle") -> int:
     """Number of admitted (query, key) pairs covered by a subset of rows.
 
     Counts mask entries element by element over the same row subsets that
@@ -233,5 +251,5 @@ def in_window_pairs(n_text: int, grid_h: int, grid_w: int, r2: int,
         ys, xs = np.arange(y0, y1 + 1), np.arange(x0, x1 + 1)
         rows = n_text + (ys[:, None] * grid_w + xs[None, :]).ravel()
         cols = _image_block_candidates(y0, y1, x0, x1, n_text, grid_h, grid_w, r2)
-        total += int(clear_mask(rows, cols, n_text, grid_w, r2).sum())
+        total += int(clear_mask(rows, cols, n_text, grid_w, r2, window).sum())
     return total

@@ -11,6 +11,9 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
   of CLEAR ("Key results") and the paper's abstract quote at 8192 x 8192.
 * ``pair_count_bruteforce`` -- the same, summed from the mask itself (small
   grids only); pins ``pair_count``.
+
+Each takes ``window="square"`` for the square-window variant
+(max(dy^2, dx^2) <= r2), where the counts are plain products.
 """
 
 from __future__ import annotations
@@ -22,16 +25,24 @@ import numpy as np
 __all__ = ["lattice_count", "pair_count", "pair_count_bruteforce"]
 
 
-def lattice_count(r2: int) -> int:
-    """#{(dy, dx) in Z^2 : dy^2 + dx^2 <= r2}, by enumerating the bounding square."""
+def _inside(dy, dx, r2, window):
+    if window == "circle":
+        return dy * dy + dx * dx <= r2
+    if window == "square":
+        return np.maximum(dy * dy, dx * dx) <= r2
+    raise ValueError(f"unknown window {window!r}")
+
+
+def lattice_count(r2: int, window: str = "circle") -> int:
+    """#{(dy, dx) in Z^2 inside the window}, by enumerating the bounding square."""
     if r2 < 0:
         return 0
     w = math.isqrt(r2)
     d = np.arange(-w, w + 1, dtype=np.int64)
-    return int(((d[:, None] ** 2 + d[None, :] ** 2) <= r2).sum())
+    return int(_inside(d[:, None], d[None, :], r2, window).sum())
 
 
-def pair_count(n_text: int, grid_h: int, grid_w: int, r2: int) -> dict:
+def pair_count(n_text: int, grid_h: int, grid_w: int, r2: int, window: str = "circle") -> dict:
     """Admitted pairs of one attention layer (one batch, one head).
 
     The image-image part enumerates the offsets (dy, dx) of the disk and counts,
@@ -44,7 +55,7 @@ def pair_count(n_text: int, grid_h: int, grid_w: int, r2: int) -> dict:
         w = math.isqrt(r2)
         for dy in range(-w, w + 1):
             for dx in range(-w, w + 1):
-                if dy * dy + dx * dx <= r2:
+                if _inside(dy, dx, r2, window):
                     img += max(0, grid_h - abs(dy)) * max(0, grid_w - abs(dx))
     n_img = grid_h * grid_w
     n = n_text + n_img
@@ -59,10 +70,11 @@ def pair_count(n_text: int, grid_h: int, grid_w: int, r2: int) -> dict:
     }
 
 
-def pair_count_bruteforce(n_text: int, grid_h: int, grid_w: int, r2: int) -> int:
+def pair_count_bruteforce(n_text: int, grid_h: int, grid_w: int, r2: int,
+                          window: str = "circle") -> int:
     """Total admitted pairs, summing the mask of every (query, key) pair."""
     from .attention import clear_mask
 
     n = n_text + grid_h * grid_w
     idx = np.arange(n)
-    return int(clear_mask(idx, idx, n_text, grid_w, r2).sum())
+    return int(clear_mask(idx, idx, n_text, grid_w, r2, window).sum())

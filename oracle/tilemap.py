@@ -1,4 +1,4 @@
-"""Tile lists of CLEAR's circular window, by brute force.
+"""Tile lists of CLEAR's circular window (and of the square variant), by brute force.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
@@ -25,6 +25,9 @@ Format (shared with the library's builders, which must match it bit for bit)
   in addition the key tile lies entirely on the grid, the sub-tile has a cell on
   the grid, and every such pair is admitted.  A key tile is listed when some bit
   0..7 is set.
+
+``window="square"`` uses the square-window predicate max(dy^2, dx^2) <= r2 of
+``oracle.attention.clear_mask`` instead.
 """
 
 from __future__ import annotations
@@ -36,9 +39,15 @@ import numpy as np
 __all__ = ["tile_map_bruteforce"]
 
 
-def _near(qy, qx, ky, kx, r2):
+def _near(qy, qx, ky, kx, r2, window="circle"):
     """Image-image part of the mask: [q, k] boolean matrix."""
-    return (qy[:, None] - ky[None, :]) ** 2 + (qx[:, None] - kx[None, :]) ** 2 <= r2
+    dy2 = (qy[:, None] - ky[None, :]) ** 2
+    dx2 = (qx[:, None] - kx[None, :]) ** 2
+    if window == "circle":
+        return dy2 + dx2 <= r2
+    if window == "square":
+        return np.maximum(dy2, dx2) <= r2
+    raise ValueError(f"unknown window {window!r}")
 
 
 def _cells(y0, x0, h, w, grid_h, grid_w):
@@ -51,14 +60,15 @@ def _cells(y0, x0, h, w, grid_h, grid_w):
 def tile_map_bruteforce(grid_h: int, grid_w: int, r2: int, tile_h: int = 16,
                         tile_w: int = 8, sub_h: int = 4, sub_w: int = 8,
                         key_h: int = 4, key_w: int = 8, tiles=None,
-                        box: bool = False) -> dict:
+                        box: bool = False, window: str = "circle") -> dict:
     """Build the tile map by evaluating the mask on every (query, key) pair.
 
     ``tiles`` restricts the output to a list of query-tile ids (offsets are then
     relative to that subset).  ``box=True`` only considers key tiles that
     intersect the query tile's bounding box widened by isqrt(r2) in each
     direction; a key tile outside that box holds no admitted key (every such key
-    has |dy| > isqrt(r2) or |dx| > isqrt(r2)), so nothing changes but the time.
+    has |dy| > isqrt(r2) or |dx| > isqrt(r2), outside either window), so nothing
+    changes but the time.
     """
     if tile_h % sub_h or tile_w % sub_w:
         raise ValueError("sub-tiles must divide the tile")
@@ -98,7 +108,7 @@ def tile_map_bruteforce(grid_h: int, grid_w: int, r2: int, tile_h: int = 16,
             for s, (qy, qx) in enumerate(subs):
                 if len(qy) == 0:
                     continue
-                m = _near(qy, qx, ky, kx, r2)
+                m = _near(qy, qx, ky, kx, r2, window)
                 if m.any():
                     f |= 1 << s
                     if on_grid and m.all():

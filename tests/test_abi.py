@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert ca.version() == 100
+    assert ca.version() == 10100  # 1.1.0: window option and the _ex tile-map entry points
 
 
 # fake, aligned, non-overlapping device addresses: validation must fail before use

@@ -23,3 +23,13 @@ def test_flux_8192_flop_counts():
     f32 = 4 * 128 * bench.admitted_pairs(512, 512, 512, 1024) * 24
     assert round(f8 / 1e12, 3) == 3.928
     assert round(f32 / 1e12, 3) == 13.097
+
+
+@pytest.mark.parametrize("n_text,gh,gw,r2", [(512, 512, 512, 1024), (512, 64, 64, 256), (7, 9, 13, 5),
+                                             (0, 5, 5, 100), (3, 4, 6, -1)])
+def test_square_admitted_pairs_match_oracle(n_text, gh, gw, r2):
+    assert bench.admitted_pairs(n_text, gh, gw, r2, "square") == \
+        pair_count(n_text, gh, gw, r2, "square")["total"]
+    if (n_text + gh * gw) <= 200:
+        assert bench.admitted_pairs(n_text, gh, gw, r2, "square") == \
+            pair_count_bruteforce(n_text, gh, gw, r2, "square")

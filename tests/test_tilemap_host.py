@@ -58,3 +58,27 @@ def test_large_grids_sampled_tiles(g, r):
         ra, rb = ref["offsets"][i], ref["offsets"][i + 1]
         np.testing.assert_array_equal(tm["key_tiles"][a:b], ref["key_tiles"][ra:rb])
         np.testing.assert_array_equal(tm["flags"][a:b], ref["flags"][ra:rb])
+
+
+@pytest.mark.parametrize("gh,gw", [(1, 9), (5, 5), (17, 9), (13, 30), (33, 24)])
+def test_square_window_small_grids(gh, gw):
+    """The square-window variant: host builder == brute force, bit for bit."""
+    for r2 in _radii(gh, gw):
+        _same(ca.tile_map_build(gh, gw, r2, window="square"),
+              tile_map_bruteforce(gh, gw, r2, window="square"))
+
+
+def test_square_window_other_tilings_and_flux_grid():
+    for th, tw, sh, sw, kh, kw in [(8, 8, 4, 4, 4, 4), (6, 9, 3, 3, 5, 2), (16, 8, 4, 8, 8, 4)]:
+        _same(ca.tile_map_build(20, 7, 17, th, tw, sh, sw, kh, kw, window="square"),
+              tile_map_bruteforce(20, 7, 17, th, tw, sh, sw, kh, kw, window="square"))
+    for r in (8, 16):
+        _same(ca.tile_map_build(64, 64, r * r, window="square"),
+              tile_map_bruteforce(64, 64, r * r, box=True, window="square"))
+
+
+def test_unknown_window_is_rejected():
+    with pytest.raises(ValueError):
+        ca.tile_map_build(8, 8, 4, window="hexagon")
+    rc = ca.lib().clear_tile_map_size_ex(7, 8, 8, 4, 16, 8, 4, 8, 4, 8, None)
+    assert rc == ca.CLEAR_EINVAL

@@ -14,22 +14,30 @@ What it computes comes from the pages about CLEAR (arXiv 2412.16112):
 * plain softmax attention with 1/sqrt(c) logit scaling (the same review,
   "Assumptions & free parameters": Eq. 1; "What carries the argument": Eq. 7);
 * text queries attend to every key (the review's referee summary: text-token
-  attention is kept global).
+  attention is kept global);
+* two variants the same pages discuss: the square window the circle is
+  inscribed in ("What carries the argument": the circle costs about pi/4 of it),
+  and the patch-averaged text rows of Eq. 7 used for multi-GPU patch-parallel
+  inference.
 
 Everything is evaluated in float64 on the exact input values.
 
 Modules
 -------
 attention  -- masked softmax attention by definition (full layer, or chosen rows)
-tilemap    -- tile lists (runs of keys per query tile, chunk flags) by brute force
+tilemap    -- tile lists (key tiles per query tile, sub-tile flags) by brute force
 counts     -- lattice-point and admitted-pair counts by enumeration
 
 Parity status: every function here has at least one pin in
-``tests/test_oracle_pins.py`` / ``tests/test_oracle_tilemap.py``.
+``tests/test_oracle_pins.py``, ``tests/test_oracle_tilemap.py``,
+``tests/test_oracle_square.py`` or ``tests/test_oracle_strips.py``.
 """
 
 from .attention import (  # noqa: F401
+    WINDOWS,
     clear_mask,
+    strip_rows,
+    text_rows_patch_average,
     attention_rows,
     attention_head,
     attention,

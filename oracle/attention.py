@@ -46,6 +46,8 @@ import numpy as np
 
 __all__ = [
     "WINDOWS",
+    "strip_rows",
+    "text_rows_patch_average",
     "clear_mask",
     "attention_rows",
     "attention_head",
@@ -253,3 +255,46 @@ def in_window_pairs(n_text: int, grid_h: int, grid_w: int, r2: int,
         cols = _image_block_candidates(y0, y1, x0, x1, n_text, grid_h, grid_w, r2)
         total += int(clear_mask(rows, cols, n_text, grid_w, r2, window).sum())
     return total
+
+
+# ---------------------------------------------------------------- patch-parallel text rows
+
+def strip_rows(grid_h: int, strips: int):
+    """Image-row ranges of `strips` horizontal patches of equal height (the last
+    ones one row taller when grid_h is not a multiple): patch p covers rows
+    floor(p * grid_h / strips) .. floor((p + 1) * grid_h / strips) - 1."""
+    if strips < 1 or strips > grid_h:
+        raise ValueError("need 1 <= strips <= grid_h")
+    return [(p * grid_h // strips, (p + 1) * grid_h // strips) for p in range(strips)]
+
+
+def text_rows_patch_average(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_text: int,
+                            grid_h: int, grid_w: int, strips: int,
+                            rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Text-query rows under the patch-wise approximation (Eq. 7 as quoted in the
+    pith.science review of CLEAR, "What carries the argument"):
+
+        O_text = (1 / N) * sum_p softmax(Q_text K_p^T / sqrt(d)) V_p
+
+    with N = `strips` horizontal image patches.  Reading: patch p's keys K_p, V_p
+    are all text tokens plus the image tokens of its rows (each device of a
+    patch-parallel run holds the text tokens and its own patch), and the softmax
+    runs over exactly those keys.  One (batch, head) slice; float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n, d = q.shape
+    if n != n_text + grid_h * grid_w:
+        raise ValueError("sequence length does not match the grid")
+    trows = np.arange(n_text) if rows is None else np.asarray(rows, dtype=np.int64)
+    if len(trows) and (trows.min() < 0 or trows.max() >= n_text):
+        raise ValueError("rows must be text rows")
+    text = np.arange(n_text, dtype=np.int64)
+    acc = np.zeros((len(trows), d))
+    for y0, y1 in strip_rows(grid_h, strips):
+        keys = np.concatenate([text, n_text + np.arange(y0 * grid_w, y1 * grid_w, dtype=np.int64)])
+        mask = np.ones((len(trows), len(keys)), dtype=bool)
+        o, _, _ = _masked_softmax_attention(q[trows], k[keys], v[keys], mask, 1.0 / math.sqrt(d))
+        acc += o
+    return acc / strips

@@ -139,6 +139,60 @@ def time_layer(ca, torch, q, k, v, w, radius, steps, warmup, window="circle"):
     }, out
 
 
+def time_strips(ca, torch, q, k, v, w, radius, strips, steps, warmup):
+    """The layer as `strips` horizontal strips (each one device's share in a
+    patch-parallel run), run one after another on this GPU, then the text rows
+    merged exactly and by the patch average (Eq. 7).  Returns per-strip and merge
+    times (HIP events on the launch stream)."""
+    B, H, N, d = q.shape
+    out = torch.empty_like(q)
+    po = torch.empty((strips, B * H, w.n_text, d), dtype=torch.float32, device=q.device)
+    pml = torch.empty((strips, B * H, w.n_text, 2), dtype=torch.float32, device=q.device)
+    rows = ca.strip_rows(w.grid_h, strips)
+    stream = torch.cuda.current_stream()
+
+    def one_pass(record=None):
+        for s_, (y0, y1) in enumerate(rows):
+            if record is not None:
+                record[s_][0].record(stream)
+            ca.fwd_strip(q, k, v, w.n_text, w.grid_h, w.grid_w, y0, y1, out, po[s_], pml[s_],
+                         radius=radius, with_text_keys=(s_ == 0))
+            if record is not None:
+                record[s_][1].record(stream)
+        if record is not None:
+            record[-2][0].record(stream)
+        ca.text_merge(po, pml, out, w.n_text, w.grid_h, w.grid_w, mode="exact")
+        if record is not None:
+            record[-2][1].record(stream)
+            record[-1][0].record(stream)
+        ca.text_merge(po, pml, out, w.n_text, w.grid_h, w.grid_w, mode="patch_average")
+        if record is not None:
+            record[-1][1].record(stream)
+
+    for _ in range(warmup):
+        one_pass()
+    times = [[0.0] * (strips + 2) for _ in range(steps)]
+    for it in range(steps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(strips + 2)]
+        one_pass(ev)
+        torch.cuda.synchronize()
+        times[it] = [a.elapsed_time(b) for a, b in ev]
+    med = [sorted(t[i] for t in times)[steps // 2] for i in range(strips + 2)]
+    halo_rows = math.isqrt(radius * radius)
+    return {
+        "strips": strips,
+        "rows_per_strip": w.grid_h // strips,
+        "strip_ms_max": round(max(med[:strips]), 4),
+        "strip_ms_min": round(min(med[:strips]), 4),
+        "strips_ms_sum": round(sum(med[:strips]), 4),
+        "merge_exact_ms": round(med[strips], 4),
+        "merge_patch_average_ms": round(med[strips + 1], 4),
+        "halo_rows_per_side": halo_rows,
+        "halo_bytes_per_neighbour": halo_rows * w.grid_w * H * d * 2 * q.element_size(),
+    }
+
+
 def cpu_baseline(q, k, v, w, radius, budget_s):
     """The fp64 oracle, untuned, on a bounded sample of the same layer: head 0,
     its first 64 text rows, then 8x8 image blocks spread over the grid until the
@@ -191,6 +245,8 @@ def main():
     ap.add_argument("--also-radius", type=int, default=8, help="second radius timed alongside (-1: none)")
     ap.add_argument("--square-radius", type=int, default=32,
                     help="also time the square-window variant at this radius (-1: none)")
+    ap.add_argument("--strips", type=int, default=8,
+                    help="also time the layer as this many horizontal strips plus text merges (0: none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -308,6 +364,11 @@ def main():
         }
     if square is not None:
         line[f"square_r{square['radius']}"] = square
+    if args.strips > 0:
+        st = time_strips(ca, torch, q, k, v, w, main_r, args.strips, min(args.steps, 10), 2)
+        line[f"strips{args.strips}"] = st
+        log(f"{args.strips} strips: max {st['strip_ms_max']:.3f} ms per strip, sum {st['strips_ms_sum']:.3f} ms, "
+            f"merges {st['merge_exact_ms']:.3f} / {st['merge_patch_average_ms']:.3f} ms")
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on a sample (~{args.cpu_seconds:.0f} s)...")
         line["cpu_baseline"] = cpu_baseline(q, k, v, w, main_r, args.cpu_seconds)

@@ -18,10 +18,10 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "ClearError", "fwd", "tile_map_size", "tile_map_build", "tile_map_build_device",
+    "ClearError", "fwd", "fwd_strip", "text_merge", "strip_rows", "tile_map_size", "tile_map_build", "tile_map_build_device",
     "release_cache", "last_error", "version", "lib", "EXPORTS",
     "CLEAR_OK", "CLEAR_EINVAL", "CLEAR_ENOMEM", "CLEAR_EHIP", "CLEAR_ENOTSUP",
-    "CLEAR_BF16", "CLEAR_FP32", "CLEAR_WINDOW_CIRCLE", "CLEAR_WINDOW_SQUARE", "WINDOWS", "TILE_H", "TILE_W", "SUB_H", "SUB_W", "KEY_H", "KEY_W", "CHUNK",
+    "CLEAR_BF16", "CLEAR_FP32", "CLEAR_MERGE_EXACT", "CLEAR_MERGE_PATCH_AVERAGE", "CLEAR_WINDOW_CIRCLE", "CLEAR_WINDOW_SQUARE", "WINDOWS", "TILE_H", "TILE_W", "SUB_H", "SUB_W", "KEY_H", "KEY_W", "CHUNK",
     "MAX_GRID",
 ]
 
@@ -30,6 +30,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libclear_at
 CLEAR_OK, CLEAR_EINVAL, CLEAR_ENOMEM, CLEAR_EHIP, CLEAR_ENOTSUP = 0, -22, -12, -5, -95
 CLEAR_BF16, CLEAR_FP32 = 0, 1
 CLEAR_WINDOW_CIRCLE, CLEAR_WINDOW_SQUARE = 0, 1
+CLEAR_MERGE_EXACT, CLEAR_MERGE_PATCH_AVERAGE = 0, 1
 WINDOWS = {"circle": CLEAR_WINDOW_CIRCLE, "square": CLEAR_WINDOW_SQUARE}
 TILE_H, TILE_W, SUB_H, SUB_W, KEY_H, KEY_W, CHUNK = 16, 8, 4, 8, 4, 8, 32
 MAX_GRID = 8192
@@ -38,7 +39,8 @@ MAX_GRID = 8192
 EXPORTS = (
     "clear_attn_fwd", "clear_attn_fwd_ex", "clear_tile_map_size", "clear_tile_map_build",
     "clear_tile_map_build_device", "clear_tile_map_size_ex", "clear_tile_map_build_ex",
-    "clear_tile_map_build_device_ex", "clear_last_error", "clear_release_cache", "clear_version",
+    "clear_tile_map_build_device_ex", "clear_attn_fwd_strip", "clear_text_merge", "clear_last_error",
+    "clear_release_cache", "clear_version",
 )
 
 
@@ -82,6 +84,10 @@ def lib():
     L.clear_tile_map_build_ex.restype = i
     L.clear_tile_map_build_device_ex.argtypes = [i] + L.clear_tile_map_build_device.argtypes
     L.clear_tile_map_build_device_ex.restype = i
+    L.clear_attn_fwd_strip.argtypes = [p, p, p, p, i, i, i, i, i, i, ctypes.POINTER(_Opts), i, i, i, p, p, p]
+    L.clear_attn_fwd_strip.restype = i
+    L.clear_text_merge.argtypes = [p, p, i, i, p, p, i, i, i, i, i, i, i, p]
+    L.clear_text_merge.restype = i
     L.clear_last_error.argtypes = []
     L.clear_last_error.restype = ctypes.c_char_p
     L.clear_release_cache.argtypes = []
@@ -176,6 +182,86 @@ def fwd(q, k, v, n_text: int, grid_h: int, grid_w: int, radius: Optional[int] = 
         rc = L.clear_attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                  B, H, d, n_text, grid_h, grid_w, ctypes.byref(opts), stream)
     _check(rc)
+    return (out, lse) if return_lse else out
+
+
+def _check_qkv(q, k, v):
+    import torch
+
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    if q.dtype == torch.bfloat16:
+        dtype = CLEAR_BF16
+    elif q.dtype == torch.float32:
+        dtype = CLEAR_FP32
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all be [B, H, N, d]")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be GPU tensors")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    return dtype
+
+
+def strip_rows(grid_h: int, strips: int):
+    """Row ranges of `strips` horizontal strips of equal height (differing by at
+    most one row): strip p covers rows p*grid_h//strips .. (p+1)*grid_h//strips - 1."""
+    if strips < 1 or strips > grid_h:
+        raise ValueError("need 1 <= strips <= grid_h")
+    return [(p * grid_h // strips, (p + 1) * grid_h // strips) for p in range(strips)]
+
+
+def fwd_strip(q, k, v, n_text: int, grid_h: int, grid_w: int, row_begin: int, row_end: int,
+              out, part_o, part_ml, radius: Optional[int] = None, r2: Optional[int] = None,
+              with_text_keys: bool = False, window: str = "circle"):
+    """One strip (image rows [row_begin, row_end)) of a patch-parallel layer:
+    writes those rows of ``out`` and the text-row partial into ``part_o``
+    [B*H, n_text, d] / ``part_ml`` [B*H, n_text, 2] (float32 GPU tensors or
+    views).  See clear_attn_fwd_strip in include/clear_attn.h."""
+    dtype = _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    if N != n_text + grid_h * grid_w:
+        raise ValueError("N != n_text + grid_h * grid_w")
+    if (radius is None) == (r2 is None):
+        raise ValueError("give exactly one of radius and r2")
+    if r2 is None:
+        r2 = min(int(radius) * int(radius), 2 ** 31 - 1)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    for t, shape in ((part_o, (B * H, n_text, d)), (part_ml, (B * H, n_text, 2))):
+        if n_text and (tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda):
+            raise ValueError(f"partial buffers must be contiguous GPU tensors of shape {shape}")
+    opts = _Opts(dtype, int(r2), None, 0, _window_code(window))
+    _check(lib().clear_attn_fwd_strip(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, d,
+                                      n_text, grid_h, grid_w, ctypes.byref(opts), row_begin, row_end,
+                                      int(bool(with_text_keys)), part_o.data_ptr() if n_text else None,
+                                      part_ml.data_ptr() if n_text else None, _stream_of(q)))
+    return out
+
+
+def text_merge(part_o, part_ml, out, n_text: int, grid_h: int, grid_w: int, mode: str = "exact",
+               return_lse: bool = False):
+    """Text rows of ``out`` [B, H, N, d] from stacked partials part_o
+    [P, B*H, n_text, d] / part_ml [P, B*H, n_text, 2]; mode "exact" (log-sum-exp)
+    or "patch_average" (the Eq. 7 text rows)."""
+    import torch
+
+    modes = {"exact": CLEAR_MERGE_EXACT, "patch_average": CLEAR_MERGE_PATCH_AVERAGE}
+    if mode not in modes:
+        raise ValueError(f"mode must be one of {sorted(modes)}")
+    B, H, N, d = out.shape
+    P = part_o.shape[0]
+    if tuple(part_o.shape) != (P, B * H, n_text, d) or tuple(part_ml.shape) != (P, B * H, n_text, 2):
+        raise ValueError("partials must be [P, B*H, n_text, d] and [P, B*H, n_text, 2]")
+    if not (part_o.is_contiguous() and part_ml.is_contiguous() and out.is_contiguous()):
+        raise ValueError("buffers must be contiguous")
+    dtype = CLEAR_BF16 if out.dtype == torch.bfloat16 else CLEAR_FP32
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=out.device) if return_lse else None
+    _check(lib().clear_text_merge(part_o.data_ptr(), part_ml.data_ptr(), P, modes[mode], out.data_ptr(),
+                                  lse.data_ptr() if lse is not None else None, B, H, d, n_text, grid_h,
+                                  grid_w, dtype, _stream_of(out)))
     return (out, lse) if return_lse else out
 
 

@@ -89,6 +89,13 @@ struct Params {
   uint64_t nkx_magic;
   int n_text_blocks, splits, chunks_per_split;
   int n_text_wg, n_text_wg_pad, n_img_wg, BH;
+  // image rows computed: [row_begin, row_end), i.e. query-tile rows
+  // band_ty0 .. band_ty0 + band_tiles / ntx - 1 (the whole grid unless a strip)
+  int row_begin, row_end, band_ty0, band_tiles;
+  // text rows: a strip's partial (text keys if strip_text_keys, then the image
+  // keys of rows [row_begin, row_end)) instead of key-range splits
+  int text_strip, strip_text_keys;
+  int partial_out;  // text workgroups write unnormalised partials (O, M, L)
   float scale_log2;
 };
 
@@ -292,14 +299,17 @@ struct F32 {
 // ---------------------------------------------------------------- key sources
 
 // Maps (chunk j, position p) to a key token for the current workgroup.
-// Chunks 0 .. n_dense-1 are a dense token range (the text keys of an image
-// tile, or a key range of a text workgroup); chunk n_dense + e is the e-th key
+// Chunks 0 .. n_dense-1 come from one or two dense token ranges (the text keys
+// of an image tile; a key range of a text workgroup; or the text keys and one
+// strip's image rows); chunk n_dense + e is the e-th key
 // tile the tile map lists for the query tile, position p = 8a + c being its
 // key cell (ky0 + a, kx0 + c).
 typedef __attribute__((address_space(4))) const uint32_t const_u32_t;
 
 struct KeySource {
-  int dense_base, dense_limit, n_dense;
+  // dense chunks 0 .. n_dense1-1 cover tokens [dense_base, dense_limit), chunks
+  // n_dense1 .. n_dense-1 cover [dense2_base, dense2_limit)
+  int dense_base, dense_limit, n_dense1, dense2_base, dense2_limit, n_dense;
   int n_text, gh, gw, nkx;
   uint64_t nkx_magic;    // ceil(2^32 / nkx): kt / nkx == (kt * magic) >> 32 here
   int e0;                // the query tile's first tile-map entry
@@ -319,6 +329,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_rsrc(const char* base, ui
 // mask needs.
 struct ChunkMeta {
   int tok0;       // first key token of the chunk
+  int limit;      // dense chunks: end of the chunk's token range
   unsigned flag;  // tile-map flags (0 for dense chunks)
   int ky0, kx0;   // key-tile origin (image chunks)
 };
@@ -326,7 +337,9 @@ struct ChunkMeta {
 __device__ __forceinline__ ChunkMeta chunk_meta(const KeySource& ks, int j) {
   ChunkMeta m;
   if (j < ks.n_dense) {
-    m.tok0 = ks.dense_base + j * kChunk;
+    const bool first = j < ks.n_dense1;
+    m.tok0 = first ? ks.dense_base + j * kChunk : ks.dense2_base + (j - ks.n_dense1) * kChunk;
+    m.limit = first ? ks.dense_limit : ks.dense2_limit;
     m.flag = 0;
     m.ky0 = 0;
     m.kx0 = 0;
@@ -338,6 +351,7 @@ __device__ __forceinline__ ChunkMeta chunk_meta(const KeySource& ks, int j) {
     m.ky0 = kty * kKeyH;
     m.kx0 = ((int)kt - kty * ks.nkx) * kKeyW;
     m.tok0 = ks.n_text + m.ky0 * ks.gw + m.kx0;
+    m.limit = 0;
   }
   return m;
 }
@@ -437,7 +451,7 @@ __device__ __forceinline__ ChunkInfo chunk_info(const ChunkMeta& m, int j, const
   ChunkInfo c{true, false, false, true, 32, m.ky0, m.kx0};
   c.square = ks.window == 1;
   if (j < ks.n_dense) {
-    const int rem = ks.dense_limit - m.tok0;
+    const int rem = m.limit - m.tok0;
     c.tail = rem < 32 ? rem : 32;
   } else {
     c.active = (m.flag >> wave) & 1u;
@@ -534,13 +548,22 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
     tq = tb * kTextQ + wave * 32 + qi;
     qvalid = tq < p.n_text;
     qtok = tq;
-    const int c0 = split * p.chunks_per_split;
-    const int nall = (p.N + kChunk - 1) / kChunk;
-    const int c1 = c0 + p.chunks_per_split < nall ? c0 + p.chunks_per_split : nall;
-    ks.dense_base = c0 * kChunk;
-    ks.dense_limit = p.N;
-    ks.n_dense = c1 - c0;
-    n_chunks = c1 - c0;
+    if (p.text_strip) {
+      ks.dense_base = 0;
+      ks.dense_limit = p.n_text;
+      ks.n_dense1 = p.strip_text_keys ? (p.n_text + kChunk - 1) / kChunk : 0;
+      ks.dense2_base = p.n_text + p.row_begin * p.gw;
+      ks.dense2_limit = p.n_text + p.row_end * p.gw;
+      ks.n_dense = ks.n_dense1 + (ks.dense2_limit - ks.dense2_base + kChunk - 1) / kChunk;
+    } else {
+      const int c0 = split * p.chunks_per_split;
+      const int nall = (p.N + kChunk - 1) / kChunk;
+      const int c1 = c0 + p.chunks_per_split < nall ? c0 + p.chunks_per_split : nall;
+      ks.dense_base = c0 * kChunk;
+      ks.dense_limit = p.N;
+      ks.n_dense1 = ks.n_dense = c1 - c0;
+    }
+    n_chunks = ks.n_dense;
   } else {
     // XCD-aware order: hardware places workgroup i on XCD i % 8.  Give each XCD
     // one contiguous range of (head, tile) so the K/V rows its tiles share stay
@@ -549,16 +572,17 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
     const int per = p.n_img_wg / 8, rem = p.n_img_wg % 8;
     const int xcd = ib % 8, slot = ib / 8;
     const int logical = xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
-    bh = logical / p.ntiles;
-    const int tile = logical - bh * p.ntiles;
-    const int ty = tile / p.ntx, tx = tile - (tile / p.ntx) * p.ntx;
+    bh = logical / p.band_tiles;
+    const int local = logical - bh * p.band_tiles;
+    const int ty = p.band_ty0 + local / p.ntx, tx = local - (local / p.ntx) * p.ntx;
+    const int tile = ty * p.ntx + tx;
     qy = ty * kTileH + wave * kSubH + (qi >> 3);
     qx = tx * kTileW + (qi & 7);
-    qvalid = qy < p.gh && qx < p.gw;
+    qvalid = qy >= p.row_begin && qy < p.row_end && qx < p.gw;
     qtok = p.n_text + qy * p.gw + qx;
     ks.dense_base = 0;
     ks.dense_limit = p.n_text;
-    ks.n_dense = (p.n_text + kChunk - 1) / kChunk;
+    ks.n_dense1 = ks.n_dense = (p.n_text + kChunk - 1) / kChunk;
     const const_u32_t* offs = (const const_u32_t*)p.tm_offsets;
     const uint32_t e0 = offs[tile];
     ks.e0 = (int)e0;
@@ -620,7 +644,7 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
   const float Lt = sum_xor32(sm.L);
   if (!qvalid) return;
   const int row = text_wg ? tq : qtok;
-  if (text_wg && p.splits > 1) {
+  if (text_wg && p.partial_out) {
     // unnormalised partial for the log-sum-exp merge
     float* wo = p.ws_o + (((size_t)split * p.BH + bh) * p.n_text + tq) * (E::kNB * 32);
     for (int nb = 0; nb < E::kNB; ++nb)
@@ -647,31 +671,71 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
   if (p.lse && g == 0) p.lse[(size_t)bh * p.N + row] = (sm.M + __log2f(Lt)) * 0.69314718055994531f;
 }
 
-// Exact merge of the text-row partials: M = max_s M_s, w_s = 2^(M_s - M),
-// O = sum_s w_s O_s / sum_s w_s L_s.
+// Text rows from partials (O_s, M_s, L_s) laid out [part][B*H][n_text][d] and
+// [part][B*H][n_text][2] (M in log2 units).
+//  * exact (log-sum-exp): M = max_s M_s, w_s = 2^(M_s - M),
+//    O = sum_s w_s O_s / sum_s w_s L_s -- softmax over the union of the parts'
+//    key sets when they partition the keys;
+//  * patch average (the patch-wise approximation of the text rows, Eq. 7 as
+//    quoted in the pith.science review of CLEAR, "What carries the argument"):
+//    O = (1/P) sum_s O_s / L_s.
+struct MergeArgs {
+  const float* po;
+  const float* pml;
+  int nparts, BH, n_text, N, mode;
+  void* out;
+  float* lse;
+};
+
 template <int D, bool BF16>
-__global__ void __launch_bounds__(D) clear_text_merge_kernel(Params p) {
+__global__ void __launch_bounds__(D) clear_text_merge_kernel(MergeArgs m) {
   const int r = blockIdx.x;  // (bh, text row)
-  const int bh = r / p.n_text, tq = r - bh * p.n_text;
+  const int bh = r / m.n_text, tq = r - bh * m.n_text;
   const int d = threadIdx.x;
-  float M = kMInit;
-  for (int s = 0; s < p.splits; ++s)
-    M = fmaxf(M, p.ws_ml[(((size_t)s * p.BH + bh) * p.n_text + tq) * 2]);
-  float L = 0.0f, acc = 0.0f;
-  for (int s = 0; s < p.splits; ++s) {
-    const size_t base = ((size_t)s * p.BH + bh) * p.n_text + tq;
-    const float w = __builtin_amdgcn_exp2f(p.ws_ml[base * 2] - M);
-    L += w * p.ws_ml[base * 2 + 1];
-    acc += w * p.ws_o[base * D + d];
-  }
-  const float o = L > 0.0f ? acc / L : 0.0f;
-  const size_t oi = ((size_t)bh * p.N + tq) * D + d;
-  if constexpr (BF16) {
-    ((__bf16*)p.out)[oi] = (__bf16)o;
+  float o;
+  if (m.mode == CLEAR_MERGE_EXACT) {
+    float M = kMInit;
+    for (int s = 0; s < m.nparts; ++s)
+      M = fmaxf(M, m.pml[(((size_t)s * m.BH + bh) * m.n_text + tq) * 2]);
+    float L = 0.0f, acc = 0.0f;
+    for (int s = 0; s < m.nparts; ++s) {
+      const size_t base = ((size_t)s * m.BH + bh) * m.n_text + tq;
+      const float w = __builtin_amdgcn_exp2f(m.pml[base * 2] - M);
+      L += w * m.pml[base * 2 + 1];
+      acc += w * m.po[base * D + d];
+    }
+    o = L > 0.0f ? acc / L : 0.0f;
+    if (m.lse && d == 0) m.lse[(size_t)bh * m.N + tq] = (M + __log2f(L)) * 0.69314718055994531f;
   } else {
-    ((float*)p.out)[oi] = o;
+    float acc = 0.0f;
+    for (int s = 0; s < m.nparts; ++s) {
+      const size_t base = ((size_t)s * m.BH + bh) * m.n_text + tq;
+      const float L = m.pml[base * 2 + 1];
+      acc += L > 0.0f ? m.po[base * D + d] / L : 0.0f;
+    }
+    o = acc / (float)m.nparts;
   }
-  if (p.lse && d == 0) p.lse[(size_t)bh * p.N + tq] = (M + __log2f(L)) * 0.69314718055994531f;
+  const size_t oi = ((size_t)bh * m.N + tq) * D + d;
+  if constexpr (BF16) {
+    ((__bf16*)m.out)[oi] = (__bf16)o;
+  } else {
+    ((float*)m.out)[oi] = o;
+  }
+}
+
+int launch_merge(const MergeArgs& m, int d, int dtype, hipStream_t s) {
+  const int rows = m.BH * m.n_text;
+  if (rows == 0) return CLEAR_OK;
+  if (dtype == CLEAR_BF16) {
+    if (d == 128) hipLaunchKernelGGL((clear_text_merge_kernel<128, true>), dim3(rows), dim3(128), 0, s, m);
+    else hipLaunchKernelGGL((clear_text_merge_kernel<64, true>), dim3(rows), dim3(64), 0, s, m);
+  } else {
+    if (d == 128) hipLaunchKernelGGL((clear_text_merge_kernel<128, false>), dim3(rows), dim3(128), 0, s, m);
+    else hipLaunchKernelGGL((clear_text_merge_kernel<64, false>), dim3(rows), dim3(64), 0, s, m);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(CLEAR_EHIP, "merge kernel launch: %s", hipGetErrorString(e));
+  return CLEAR_OK;
 }
 
 template <class E>
@@ -681,6 +745,12 @@ int launch_main(const Params& p, hipStream_t s, int grid) {
 }
 
 }  // namespace
+
+int text_merge_launch(const float* part_o, const float* part_ml, int nparts, int mode, void* out,
+                      float* lse, int BH, int n_text, int N, int d, int dtype, void* stream) {
+  MergeArgs m{part_o, part_ml, nparts, BH, n_text, N, mode, out, lse};
+  return launch_merge(m, d, dtype, (hipStream_t)stream);
+}
 
 int attn_launch(const AttnLaunch& a, void* stream) {
   hipStream_t s = (hipStream_t)stream;
@@ -710,15 +780,22 @@ int attn_launch(const AttnLaunch& a, void* stream) {
   p.n_text_blocks = (a.n_text + kTextQ - 1) / kTextQ;
   const int nall = (p.N + kChunk - 1) / kChunk;
   int splits = a.text_splits < 1 ? 1 : a.text_splits;
-  if (splits > nall) splits = nall;
+  if (splits > nall || a.strip) splits = a.strip ? 1 : nall;
   p.chunks_per_split = (nall + splits - 1) / splits;
   p.splits = (nall + p.chunks_per_split - 1) / p.chunks_per_split;  // no empty split
+  p.text_strip = a.strip;
+  p.strip_text_keys = a.strip_text_keys;
+  p.partial_out = a.strip || p.splits > 1;
   p.n_text_wg = p.BH * p.n_text_blocks * p.splits;
   p.n_text_wg_pad = (p.n_text_wg + 7) / 8 * 8;
-  p.n_img_wg = p.BH * p.ntiles;
+  p.row_begin = a.row_begin;
+  p.row_end = a.row_end;
+  p.band_ty0 = a.row_begin / kTileH;
+  p.band_tiles = ((a.row_end + kTileH - 1) / kTileH - p.band_ty0) * p.ntx;
+  p.n_img_wg = p.BH * p.band_tiles;
   p.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)a.d));
-  if (p.splits > 1 && (!a.ws_o || !a.ws_ml))
-    return set_error(CLEAR_EINVAL, "text splits > 1 need a workspace");
+  if (p.partial_out && p.n_text > 0 && (!a.ws_o || !a.ws_ml))
+    return set_error(CLEAR_EINVAL, "text partials need a workspace");
   const long long grid = (long long)p.n_text_wg_pad + p.n_img_wg;
   if (grid > 0x7fffffffLL) return set_error(CLEAR_EINVAL, "too many workgroups");
 
@@ -729,17 +806,10 @@ int attn_launch(const AttnLaunch& a, void* stream) {
     rc = a.d == 128 ? launch_main<F32<128>>(p, s, (int)grid) : launch_main<F32<64>>(p, s, (int)grid);
   }
   if (rc) return set_error(CLEAR_EHIP, "attention kernel launch: %s", hipGetErrorString(hipGetLastError()));
-  if (p.splits > 1 && p.n_text > 0) {
-    const int rows = p.BH * p.n_text;
-    if (a.dtype == CLEAR_BF16) {
-      if (a.d == 128) hipLaunchKernelGGL((clear_text_merge_kernel<128, true>), dim3(rows), dim3(128), 0, s, p);
-      else hipLaunchKernelGGL((clear_text_merge_kernel<64, true>), dim3(rows), dim3(64), 0, s, p);
-    } else {
-      if (a.d == 128) hipLaunchKernelGGL((clear_text_merge_kernel<128, false>), dim3(rows), dim3(128), 0, s, p);
-      else hipLaunchKernelGGL((clear_text_merge_kernel<64, false>), dim3(rows), dim3(64), 0, s, p);
-    }
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return set_error(CLEAR_EHIP, "merge kernel launch: %s", hipGetErrorString(e));
+  if (!a.strip && p.splits > 1 && p.n_text > 0) {
+    MergeArgs m{p.ws_o, p.ws_ml, p.splits, p.BH, p.n_text, p.N, CLEAR_MERGE_EXACT, p.out, p.lse};
+    rc = launch_merge(m, a.d, a.dtype, s);
+    if (rc) return rc;
   }
   return CLEAR_OK;
 }

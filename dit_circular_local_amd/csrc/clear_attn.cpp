@@ -134,12 +134,22 @@ using namespace clear;
 
 extern "C" const char* clear_last_error(void) { return g_err; }
 
-extern "C" int clear_version(void) { return 10100; }
+extern "C" int clear_version(void) { return 10200; }
 
-extern "C" int clear_attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B,
-                                 int H, int d, int n_text, int grid_h, int grid_w,
-                                 const clear_opts* opts, void* stream) {
-  clear_error_reset();
+namespace {
+
+// The forward pass behind clear_attn_fwd_ex (whole layer: strip == nullptr) and
+// clear_attn_fwd_strip (one strip: image rows [row_begin, row_end) and the text
+// partial into the caller's buffers).
+struct StripArgs {
+  int row_begin, row_end, text_keys;
+  float* part_o;
+  float* part_ml;
+};
+
+int run_forward(const void* q, const void* k, const void* v, void* out, int B, int H, int d,
+                int n_text, int grid_h, int grid_w, const clear_opts* opts, const StripArgs* strip,
+                void* stream) {
   clear_opts o = opts ? *opts : clear_opts{CLEAR_BF16, 0, nullptr, 0, CLEAR_WINDOW_CIRCLE};
   if (!q || !k || !v || !out) return set_error(CLEAR_EINVAL, "q, k, v and out must not be NULL");
   if (B < 1 || H < 1) return set_error(CLEAR_EINVAL, "B and H must be >= 1 (got %d, %d)", B, H);
@@ -157,6 +167,16 @@ extern "C" int clear_attn_fwd_ex(const void* q, const void* k, const void* v, vo
     return set_error(CLEAR_EINVAL, "n_text == 0 and r2_max < 0: every query row would be empty");
   if (o.text_splits < 0 || o.text_splits > 64)
     return set_error(CLEAR_EINVAL, "text_splits must be in 0..64 (got %d)", o.text_splits);
+  if (strip) {
+    if (strip->row_begin < 0 || strip->row_end > grid_h || strip->row_begin >= strip->row_end)
+      return set_error(CLEAR_EINVAL, "strip rows [%d, %d) must be a non-empty range inside 0..%d",
+                       strip->row_begin, strip->row_end, grid_h);
+    if (o.text_splits != 0) return set_error(CLEAR_EINVAL, "a strip computes its text partial in one part");
+    if (n_text > 0 && (!strip->part_o || !strip->part_ml))
+      return set_error(CLEAR_EINVAL, "text_part_o and text_part_ml must not be NULL when n_text > 0");
+    if (((uintptr_t)strip->part_o | (uintptr_t)strip->part_ml) & 3)
+      return set_error(CLEAR_EINVAL, "text partial buffers must be 4-byte aligned");
+  }
   const long long N = (long long)n_text + (long long)grid_h * grid_w;
   if (N > 0x7fffffffLL) return set_error(CLEAR_EINVAL, "sequence too long");
   const size_t elem = o.dtype == CLEAR_BF16 ? 2 : 4;
@@ -182,15 +202,23 @@ extern "C" int clear_attn_fwd_ex(const void* q, const void* k, const void* v, vo
 
   TileGeom g = make_geom(grid_h, grid_w, o.r2_max, CLEAR_TILE_H, CLEAR_TILE_W, CLEAR_SUB_H, CLEAR_SUB_W,
                          CLEAR_KEY_H, CLEAR_KEY_W, o.window);
-  int splits = o.text_splits ? o.text_splits
-                             : choose_text_splits(B, H, n_text, (int)N, g.nty * g.ntx, tm->n_entries);
+  int splits = strip ? 1
+                     : o.text_splits ? o.text_splits
+                                     : choose_text_splits(B, H, n_text, (int)N, g.nty * g.ntx, tm->n_entries);
   AttnLaunch a;
   memset(&a, 0, sizeof a);
   a.q = q; a.k = k; a.v = v; a.out = out; a.lse = o.lse_out;
   a.tm_offsets = tm->offsets; a.tm_key_tiles = tm->key_tiles; a.tm_flags = tm->flags;
   a.B = B; a.H = H; a.d = d; a.n_text = n_text; a.gh = grid_h; a.gw = grid_w; a.r2 = g.r2;
   a.dtype = o.dtype; a.text_splits = splits; a.window = o.window;
-  if (splits > 1 && n_text > 0) {
+  a.row_begin = strip ? strip->row_begin : 0;
+  a.row_end = strip ? strip->row_end : grid_h;
+  if (strip) {
+    a.strip = 1;
+    a.strip_text_keys = strip->text_keys ? 1 : 0;
+    a.ws_o = strip->part_o;
+    a.ws_ml = strip->part_ml;
+  } else if (splits > 1 && n_text > 0) {
     const size_t o_bytes = align_up((size_t)splits * B * H * n_text * d * 4, 256);
     const size_t need = o_bytes + (size_t)splits * B * H * n_text * 2 * 4;
     if (need > ds.ws_bytes) {
@@ -213,6 +241,54 @@ extern "C" int clear_attn_fwd_ex(const void* q, const void* k, const void* v, vo
   if (debug_sync_enabled()) {
     if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "CLEAR_DEBUG sync");
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "CLEAR_DEBUG check");
+  }
+  return CLEAR_OK;
+}
+
+}  // namespace
+
+extern "C" int clear_attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B,
+                                 int H, int d, int n_text, int grid_h, int grid_w,
+                                 const clear_opts* opts, void* stream) {
+  clear_error_reset();
+  return run_forward(q, k, v, out, B, H, d, n_text, grid_h, grid_w, opts, nullptr, stream);
+}
+
+extern "C" int clear_attn_fwd_strip(const void* q, const void* k, const void* v, void* out, int B,
+                                    int H, int d, int n_text, int grid_h, int grid_w,
+                                    const clear_opts* opts, int row_begin, int row_end,
+                                    int with_text_keys, float* text_part_o, float* text_part_ml,
+                                    void* stream) {
+  clear_error_reset();
+  StripArgs st{row_begin, row_end, with_text_keys, text_part_o, text_part_ml};
+  return run_forward(q, k, v, out, B, H, d, n_text, grid_h, grid_w, opts, &st, stream);
+}
+
+extern "C" int clear_text_merge(const float* part_o, const float* part_ml, int nparts, int mode,
+                                void* out, float* lse_out, int B, int H, int d, int n_text,
+                                int grid_h, int grid_w, int dtype, void* stream) {
+  clear_error_reset();
+  if (!part_o || !part_ml || !out) return set_error(CLEAR_EINVAL, "part_o, part_ml and out must not be NULL");
+  if (nparts < 1) return set_error(CLEAR_EINVAL, "nparts must be >= 1 (got %d)", nparts);
+  if (mode != CLEAR_MERGE_EXACT && mode != CLEAR_MERGE_PATCH_AVERAGE)
+    return set_error(CLEAR_EINVAL, "mode must be CLEAR_MERGE_EXACT or CLEAR_MERGE_PATCH_AVERAGE (got %d)", mode);
+  if (mode == CLEAR_MERGE_PATCH_AVERAGE && lse_out)
+    return set_error(CLEAR_EINVAL, "the patch average has no log-sum-exp; pass lse_out = NULL");
+  if (B < 1 || H < 1) return set_error(CLEAR_EINVAL, "B and H must be >= 1 (got %d, %d)", B, H);
+  if (d != 64 && d != 128) return set_error(CLEAR_EINVAL, "d must be 64 or 128 (got %d)", d);
+  if (n_text < 0) return set_error(CLEAR_EINVAL, "n_text must be >= 0 (got %d)", n_text);
+  if (grid_h < 1 || grid_w < 1 || grid_h > CLEAR_MAX_GRID || grid_w > CLEAR_MAX_GRID)
+    return set_error(CLEAR_EINVAL, "grid sides must be in 1..%d (got %d x %d)", CLEAR_MAX_GRID, grid_h, grid_w);
+  if (dtype != CLEAR_BF16 && dtype != CLEAR_FP32)
+    return set_error(CLEAR_EINVAL, "dtype must be CLEAR_BF16 or CLEAR_FP32 (got %d)", dtype);
+  const long long N = (long long)n_text + (long long)grid_h * grid_w;
+  if (N > 0x7fffffffLL) return set_error(CLEAR_EINVAL, "sequence too long");
+  int rc = text_merge_launch(part_o, part_ml, nparts, mode, out, lse_out, B * H, n_text, (int)N, d,
+                             dtype, stream);
+  if (rc) return rc;
+  if (debug_sync_enabled()) {
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "CLEAR_DEBUG sync");
   }
   return CLEAR_OK;
 }

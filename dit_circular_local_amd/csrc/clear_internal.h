@@ -40,8 +40,13 @@ struct AttnLaunch {
   int dtype;
   int text_splits;
   int window;                 // CLEAR_WINDOW_CIRCLE or CLEAR_WINDOW_SQUARE
+  int row_begin, row_end;     // image rows computed (0, gh for the whole layer)
+  int strip;                  // text rows: write the strip's partial to ws_o / ws_ml
+  int strip_text_keys;        //   ... including the text keys
 };
 
 int attn_launch(const AttnLaunch& a, void* stream);
+int text_merge_launch(const float* part_o, const float* part_ml, int nparts, int mode, void* out,
+                      float* lse, int BH, int n_text, int N, int d, int dtype, void* stream);
 
 }  // namespace clear

@@ -60,6 +60,9 @@ extern "C" {
 #define CLEAR_WINDOW_CIRCLE 0  /* dy^2 + dx^2 <= r2 (CLEAR)      */
 #define CLEAR_WINDOW_SQUARE 1  /* max(dy^2, dx^2) <= r2 (variant) */
 
+#define CLEAR_MERGE_EXACT 0          /* log-sum-exp merge of text-row partials      */
+#define CLEAR_MERGE_PATCH_AVERAGE 1  /* mean of normalised partials (Eq. 7 reading) */
+
 /* Tiling of the attention kernels: a workgroup owns a 16 x 8 cell query tile;
  * each of its four wavefronts owns a 4 x 8 sub-tile; image keys stream in 4 x 8
  * cell key tiles (32 keys), text keys in chunks of 32.  clear_tile_map_build*
@@ -118,6 +121,56 @@ int clear_attn_fwd(const void* q, const void* k, const void* v, void* out,
 int clear_attn_fwd_ex(const void* q, const void* k, const void* v, void* out,
                       int B, int H, int d, int n_text, int grid_h, int grid_w,
                       const clear_opts* opts, void* stream);
+
+/*
+ * clear_attn_fwd_strip -- one horizontal strip of a patch-parallel layer: the
+ * share of one device when the image grid is split into row strips (the pages'
+ * patch-parallel inference; pith.science review, "What carries the argument").
+ *
+ *   q, k, v, out, B, H, d, n_text, grid_h, grid_w, opts: as clear_attn_fwd_ex
+ *     (opts->text_splits must be 0; opts->lse_out, if set, receives the LSE of
+ *     the strip's image rows only).
+ *   row_begin, row_end : the strip, image rows [row_begin, row_end), 0 <= row_begin
+ *     < row_end <= grid_h.  Exactly those image rows of out are written (text
+ *     rows and other image rows are left untouched).  Their keys are the text
+ *     tokens and the image rows within isqrt(r2_max) of the strip: the strip plus
+ *     halos of O(r x grid_w) keys, as on a device holding only that slab.
+ *   with_text_keys : nonzero = the text-row partial also covers the text keys.
+ *   text_part_o  : device, [B*H, n_text, d] float32 -- unnormalised partial
+ *                  O_s = sum_j 2^(c s_j - M_s) v_j over the strip's keys for the text
+ *                  rows (c = log2(e)/sqrt(d), s_j = q.k_j);
+ *   text_part_ml : device, [B*H, n_text, 2] float32 -- (M_s, L_s), M_s the reference
+ *                  max in log2 units, L_s = sum_j 2^(c s_j - M_s).
+ *                  The partial's keys: text keys if with_text_keys, then the image
+ *                  tokens of rows [row_begin, row_end).  Both buffers caller-owned,
+ *                  4-byte aligned; NULL allowed when n_text == 0.
+ * Merging the partials of strips that cover all rows, exactly one of them with
+ * text keys, with CLEAR_MERGE_EXACT reproduces the text rows of clear_attn_fwd_ex.
+ */
+int clear_attn_fwd_strip(const void* q, const void* k, const void* v, void* out,
+                         int B, int H, int d, int n_text, int grid_h, int grid_w,
+                         const clear_opts* opts, int row_begin, int row_end,
+                         int with_text_keys, float* text_part_o, float* text_part_ml,
+                         void* stream);
+
+/*
+ * clear_text_merge -- text rows of out from nparts text-row partials stacked as
+ * [nparts][B*H][n_text][d] and [nparts][B*H][n_text][2] (the layout written by
+ * clear_attn_fwd_strip; consecutive strips' buffers).
+ *   mode CLEAR_MERGE_EXACT: M = max_s M_s, w_s = 2^(M_s - M),
+ *        O = sum_s w_s O_s / sum_s w_s L_s (softmax over the union of the parts'
+ *        keys; exact when they partition the keys); lse_out (optional, device
+ *        [B, H, N] float32) receives the natural-log LSE of the text rows.
+ *   mode CLEAR_MERGE_PATCH_AVERAGE: O = (1/nparts) sum_s O_s / L_s, the
+ *        patch-wise text-row approximation (Eq. 7 as quoted in the pith.science
+ *        review, "What carries the argument"), with each part the softmax over its
+ *        device's keys; lse_out must be NULL.
+ *   out: device [B, H, N, d] (N = n_text + grid_h*grid_w) of dtype; only rows
+ *        0 .. n_text-1 are written.
+ */
+int clear_text_merge(const float* part_o, const float* part_ml, int nparts, int mode,
+                     void* out, float* lse_out, int B, int H, int d, int n_text,
+                     int grid_h, int grid_w, int dtype, void* stream);
 
 /*
  * clear_tile_map_size -- number of entries of the tile map (host, closed form).

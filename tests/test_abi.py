@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert ca.version() == 10100  # 1.1.0: window option and the _ex tile-map entry points
+    assert ca.version() == 10200  # 1.2.0: strips and text-row merging
 
 
 # fake, aligned, non-overlapping device addresses: validation must fail before use

@@ -1,0 +1,121 @@
+"""GPU: the layer computed as horizontal strips (one device's share each in a
+patch-parallel run), text rows merged exactly or by the patch average of Eq. 7
+(pith.science review of CLEAR, "What carries the argument")."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import dit_circular_local_amd as ca
+from dit_circular_local_amd.inputs import make_qkv
+from oracle import attention, text_rows_patch_average
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-5, "bf16": 2e-2}
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _inputs(dtype, B, H, n_text, gh, gw, d, seed):
+    return make_qkv(B, H, n_text, gh, gw, d, dtype, seed, rms_norm=(dtype == "bf16"),
+                    scale=1.0 if dtype == "bf16" else 1.0 / math.sqrt(d), device="cuda")
+
+
+def _run_strips(q, k, v, n_text, gh, gw, r2, P, text_keys_everywhere, window="circle"):
+    B, H, N, d = q.shape
+    out = torch.full_like(q, float("nan"))
+    po = torch.zeros((P, B * H, max(n_text, 1), d), dtype=torch.float32, device="cuda")[:, :, :n_text]
+    pml = torch.zeros((P, B * H, max(n_text, 1), 2), dtype=torch.float32, device="cuda")[:, :, :n_text]
+    po, pml = po.contiguous(), pml.contiguous()
+    for s, (y0, y1) in enumerate(ca.strip_rows(gh, P)):
+        ca.fwd_strip(q, k, v, n_text, gh, gw, y0, y1, out, po[s], pml[s], r2=r2,
+                     with_text_keys=text_keys_everywhere or s == 0, window=window)
+    return out, po, pml
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("P", [1, 2, 3, 5])
+def test_strips_reproduce_the_layer(dtype, P):
+    n_text, gh, gw, d, r2 = 130, 45, 24, 128, 49
+    q, k, v = _inputs(dtype, 1, 2, n_text, gh, gw, d, seed=P)
+    full = ca.fwd(q, k, v, n_text, gh, gw, r2=r2)
+    out, po, pml = _run_strips(q, k, v, n_text, gh, gw, r2, P, text_keys_everywhere=False)
+    ca.text_merge(po, pml, out, n_text, gh, gw, mode="exact")
+    torch.cuda.synchronize()
+    # image rows: the same tiles and chunk order as the whole-layer launch
+    assert torch.equal(out[:, :, n_text:], full[:, :, n_text:])
+    ref, _ = attention(_np(q), _np(k), _np(v), n_text, gh, gw, r2, workers=4)
+    err = np.abs(_np(out) - ref).max()
+    assert err <= TOL[dtype], f"{dtype} P={P}: max-abs {err:.3e}"
+
+
+@pytest.mark.parametrize("dtype,P", [("fp32", 2), ("fp32", 4), ("bf16", 3), ("bf16", 8)])
+def test_patch_average_text_rows_match_eq7(dtype, P):
+    n_text, gh, gw, d, r2 = 64, 32, 16, 128, 16
+    q, k, v = _inputs(dtype, 1, 2, n_text, gh, gw, d, seed=10 + P)
+    out, po, pml = _run_strips(q, k, v, n_text, gh, gw, r2, P, text_keys_everywhere=True)
+    ca.text_merge(po, pml, out, n_text, gh, gw, mode="patch_average")
+    torch.cuda.synchronize()
+    for h in range(2):
+        ref = text_rows_patch_average(_np(q[0, h]), _np(k[0, h]), _np(v[0, h]), n_text, gh, gw, P)
+        err = np.abs(_np(out[0, h, :n_text]) - ref).max()
+        assert err <= TOL[dtype], f"{dtype} P={P} head {h}: max-abs {err:.3e}"
+
+
+def test_exact_merge_lse_and_one_strip_with_text_keys_only_once():
+    n_text, gh, gw, d, r2 = 40, 20, 20, 64, 25
+    q, k, v = _inputs("fp32", 2, 1, n_text, gh, gw, d, seed=21)
+    out, po, pml = _run_strips(q, k, v, n_text, gh, gw, r2, 4, text_keys_everywhere=False)
+    _, lse = ca.text_merge(po, pml, out, n_text, gh, gw, mode="exact", return_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = attention(_np(q), _np(k), _np(v), n_text, gh, gw, r2)
+    assert np.abs(_np(lse[:, :, :n_text]) - ref_lse[:, :, :n_text]).max() <= 1e-5
+
+
+@pytest.mark.parametrize("window", ["circle", "square"])
+def test_strip_reads_only_its_halo(window):
+    """Keys more than isqrt(r2) rows away from the strip do not change its rows:
+    poisoning them (large finite values) leaves the strip's outputs bit-identical."""
+    n_text, gh, gw, d, r2 = 16, 48, 24, 128, 36
+    q, k, v = _inputs("bf16", 1, 2, n_text, gh, gw, d, seed=31)
+    y0, y1 = 16, 29
+    w = math.isqrt(r2)
+    out_a, po_a, pml_a = (torch.zeros_like(q), torch.zeros((2, n_text, d), device="cuda"),
+                          torch.zeros((2, n_text, 2), device="cuda"))
+    ca.fwd_strip(q, k, v, n_text, gh, gw, y0, y1, out_a, po_a, pml_a, r2=r2, window=window)
+    k2, v2 = k.clone(), v.clone()
+    far = [y for y in range(gh) if y < y0 - w or y >= y1 + w]
+    for y in far:
+        s = n_text + y * gw
+        k2[:, :, s:s + gw] = 300.0
+        v2[:, :, s:s + gw] = -500.0
+    out_b, po_b, pml_b = torch.zeros_like(q), torch.zeros_like(po_a), torch.zeros_like(pml_a)
+    ca.fwd_strip(q, k2, v2, n_text, gh, gw, y0, y1, out_b, po_b, pml_b, r2=r2, window=window)
+    torch.cuda.synchronize()
+    rows = slice(n_text + y0 * gw, n_text + y1 * gw)
+    assert torch.equal(out_a[:, :, rows], out_b[:, :, rows])
+    # the text partial covers only the strip's own rows: unaffected as well
+    assert torch.equal(po_a, po_b) and torch.equal(pml_a, pml_b)
+
+
+def test_strip_and_merge_reject_bad_arguments():
+    n_text, gh, gw, d = 8, 8, 8, 64
+    q, k, v = _inputs("bf16", 1, 1, n_text, gh, gw, d, seed=1)
+    out = torch.zeros_like(q)
+    po, pml = torch.zeros((1, n_text, d), device="cuda"), torch.zeros((1, n_text, 2), device="cuda")
+    for y0, y1 in [(3, 3), (-1, 4), (2, 9)]:
+        with pytest.raises(ca.ClearError) as e:
+            ca.fwd_strip(q, k, v, n_text, gh, gw, y0, y1, out, po, pml, radius=2)
+        assert e.value.code == ca.CLEAR_EINVAL
+    L = ca.lib()
+    rc = L.clear_text_merge(po.data_ptr(), pml.data_ptr(), 1, ca.CLEAR_MERGE_PATCH_AVERAGE, out.data_ptr(),
+                            po.data_ptr(), 1, 1, d, n_text, gh, gw, ca.CLEAR_BF16, None)
+    assert rc == ca.CLEAR_EINVAL and "lse" in ca.last_error()
+    rc = L.clear_text_merge(po.data_ptr(), pml.data_ptr(), 0, ca.CLEAR_MERGE_EXACT, out.data_ptr(),
+                            None, 1, 1, d, n_text, gh, gw, ca.CLEAR_BF16, None)
+    assert rc == ca.CLEAR_EINVAL

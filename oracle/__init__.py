@@ -18,19 +18,23 @@ What it computes comes from the pages about CLEAR (arXiv 2412.16112):
 * two variants the same pages discuss: the square window the circle is
   inscribed in ("What carries the argument": the circle costs about pi/4 of it),
   and the patch-averaged text rows of Eq. 7 used for multi-GPU patch-parallel
-  inference.
+  inference;
+* the gradients of that attention (dQ, dK, dV), the step that follows it in the
+  paper's attention-only distillation fine-tuning, by the chain rule.
 
 Everything is evaluated in float64 on the exact input values.
 
 Modules
 -------
 attention  -- masked softmax attention by definition (full layer, or chosen rows)
+backward   -- its gradients by the chain rule (full layer, chosen query rows or keys)
 tilemap    -- tile lists (key tiles per query tile, sub-tile flags) by brute force
 counts     -- lattice-point and admitted-pair counts by enumeration
 
 Parity status: every function here has at least one pin in
 ``tests/test_oracle_pins.py``, ``tests/test_oracle_tilemap.py``,
-``tests/test_oracle_square.py`` or ``tests/test_oracle_strips.py``.
+``tests/test_oracle_square.py``, ``tests/test_oracle_strips.py`` or
+``tests/test_oracle_backward.py``.
 """
 
 from .attention import (  # noqa: F401
@@ -43,5 +47,6 @@ from .attention import (  # noqa: F401
     attention,
     in_window_pairs,
 )
+from .backward import attention_backward, attention_backward_head, key_grads  # noqa: F401
 from .tilemap import tile_map_bruteforce  # noqa: F401
 from .counts import lattice_count, pair_count, pair_count_bruteforce  # noqa: F401

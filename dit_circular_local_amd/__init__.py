@@ -18,7 +18,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "ClearError", "fwd", "fwd_strip", "text_merge", "strip_rows", "tile_map_size", "tile_map_build", "tile_map_build_device",
+    "ClearError", "fwd", "bwd", "fwd_strip", "text_merge", "strip_rows", "tile_map_size", "tile_map_build", "tile_map_build_device",
     "release_cache", "last_error", "version", "lib", "EXPORTS",
     "CLEAR_OK", "CLEAR_EINVAL", "CLEAR_ENOMEM", "CLEAR_EHIP", "CLEAR_ENOTSUP",
     "CLEAR_BF16", "CLEAR_FP32", "CLEAR_MERGE_EXACT", "CLEAR_MERGE_PATCH_AVERAGE", "CLEAR_WINDOW_CIRCLE", "CLEAR_WINDOW_SQUARE", "WINDOWS", "TILE_H", "TILE_W", "SUB_H", "SUB_W", "KEY_H", "KEY_W", "CHUNK",
@@ -39,7 +39,8 @@ MAX_GRID = 8192
 EXPORTS = (
     "clear_attn_fwd", "clear_attn_fwd_ex", "clear_tile_map_size", "clear_tile_map_build",
     "clear_tile_map_build_device", "clear_tile_map_size_ex", "clear_tile_map_build_ex",
-    "clear_tile_map_build_device_ex", "clear_attn_fwd_strip", "clear_text_merge", "clear_last_error",
+    "clear_tile_map_build_device_ex", "clear_attn_fwd_strip", "clear_text_merge", "clear_attn_bwd",
+    "clear_last_error",
     "clear_release_cache", "clear_version",
 )
 
@@ -88,6 +89,8 @@ def lib():
     L.clear_attn_fwd_strip.restype = i
     L.clear_text_merge.argtypes = [p, p, i, i, p, p, i, i, i, i, i, i, i, p]
     L.clear_text_merge.restype = i
+    L.clear_attn_bwd.argtypes = [p, p, p, p, p, p, p, p, p, i, i, i, i, i, i, ctypes.POINTER(_Opts), p]
+    L.clear_attn_bwd.restype = i
     L.clear_last_error.argtypes = []
     L.clear_last_error.restype = ctypes.c_char_p
     L.clear_release_cache.argtypes = []
@@ -203,6 +206,43 @@ def _check_qkv(q, k, v):
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous")
     return dtype
+
+
+def bwd(q, k, v, out, dout, lse, n_text: int, grid_h: int, grid_w: int, radius: Optional[int] = None,
+        r2: Optional[int] = None, text_splits: int = 0, window: str = "circle", grads=None):
+    """Gradients (dq, dk, dv) of the CLEAR attention layer for upstream gradient
+    ``dout``, given the forward's inputs, its output ``out`` and its ``lse``
+    (``fwd(..., return_lse=True)``).  Same options as ``fwd``; ``grads`` may
+    pass preallocated (dq, dk, dv).  See clear_attn_bwd in include/clear_attn.h."""
+    import torch
+
+    dtype = _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    if N != n_text + grid_h * grid_w:
+        raise ValueError(f"N = {N} != n_text + grid_h * grid_w = {n_text + grid_h * grid_w}")
+    for name, t in (("out", out), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous GPU tensor shaped and typed like q")
+    if (tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous()
+            or not lse.is_cuda):
+        raise ValueError("lse must be a contiguous float32 GPU tensor [B, H, N]")
+    if (radius is None) == (r2 is None):
+        raise ValueError("give exactly one of radius and r2")
+    if r2 is None:
+        if radius < 0:
+            raise ValueError("radius must be >= 0")
+        r2 = min(int(radius) * int(radius), 2 ** 31 - 1)
+    if grads is None:
+        grads = tuple(torch.empty_like(q) for _ in range(3))
+    for t in grads:
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("dq, dk, dv must be contiguous tensors shaped and typed like q")
+    dq, dk, dv = grads
+    opts = _Opts(dtype, int(r2), None, int(text_splits), _window_code(window))
+    _check(lib().clear_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, d, n_text,
+                                grid_h, grid_w, ctypes.byref(opts), _stream_of(q)))
+    return dq, dk, dv
 
 
 def strip_rows(grid_h: int, strips: int):

@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libclear_attn.so")
 
-SOURCES = ["clear_attn.cpp", "tilemap_host.cpp", "tilemap_device.hip", "attn_fwd.hip"]
+SOURCES = ["clear_attn.cpp", "tilemap_host.cpp", "tilemap_device.hip", "attn_fwd.hip", "attn_bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

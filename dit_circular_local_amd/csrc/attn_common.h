@@ -1,0 +1,185 @@
+// attn_common.h -- device code shared by the attention kernels (forward and
+// backward): vector types, tile geometry, the 32x32 MFMA accumulator layout,
+// the walk over a workgroup's chunks (dense token ranges, then the 4 x 8 cell
+// tiles the tile map lists for its tile) and the per-element window mask.
+//
+// The mask is CLEAR's (pith.science review of arXiv 2412.16112, "Core claim"):
+// a pair is admitted when either token is text or the two image cells are
+// within radius r; the square window of "What carries the argument" replaces
+// the distance by max(dy^2, dx^2).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "clear_internal.h"
+
+namespace clear {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+typedef __attribute__((ext_vector_type(2))) short s16x2_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((ext_vector_type(8))) short s16x8_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kTileH = CLEAR_TILE_H;
+constexpr int kTileW = CLEAR_TILE_W;
+constexpr int kSubH = CLEAR_SUB_H;
+constexpr int kChunk = CLEAR_CHUNK;
+constexpr int kKeyH = CLEAR_KEY_H;
+constexpr int kKeyW = CLEAR_KEY_W;
+
+static_assert(kTileH == kWaves * kSubH && kTileW == CLEAR_SUB_W && kTileW * kSubH == 32,
+              "one 32-query sub-tile per wavefront");
+static_assert(kChunk == 32, "chunk = one 32-row MFMA block");
+static_assert(kKeyH * kKeyW == kChunk && kKeyW == 8,
+              "key tile = one chunk; key cell (a, c) is chunk position 8a + c");
+
+
+// Key position m (0..31) of accumulator register i in lane group g: the row
+// index of the 32x32 accumulator layout.
+__device__ __forceinline__ int acc_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
+
+// Wave-wide combine of a value with its partner lane l ^ 32.
+__device__ __forceinline__ float max_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---------------------------------------------------------------- key sources
+
+// Maps (chunk j, position p) to a key token for the current workgroup.
+// Chunks 0 .. n_dense-1 come from one or two dense token ranges (the text keys
+// of an image tile; a key range of a text workgroup; or the text keys and one
+// strip's image rows); chunk n_dense + e is the e-th key
+// tile the tile map lists for the query tile, position p = 8a + c being its
+// key cell (ky0 + a, kx0 + c).
+typedef __attribute__((address_space(4))) const uint32_t const_u32_t;
+
+struct KeySource {
+  // dense chunks 0 .. n_dense1-1 cover tokens [dense_base, dense_limit), chunks
+  // n_dense1 .. n_dense-1 cover [dense2_base, dense2_limit)
+  int dense_base, dense_limit, n_dense1, dense2_base, dense2_limit, n_dense;
+  int n_text, gh, gw, nkx;
+  uint64_t nkx_magic;    // ceil(2^32 / nkx): kt / nkx == (kt * magic) >> 32 here
+  int e0;                // the query tile's first tile-map entry
+  int window;            // 0 circle, 1 square
+  int n_tok;             // tokens per head (N)
+  const_u32_t* key_tiles;  // whole tile map, read through the scalar cache
+  const_u32_t* flags32;    // u16 flags, two per word
+};
+
+// Buffer resource over `bytes` bytes from a uniform address (gfx9 resource
+// word 3).  Loads at offsets >= bytes return zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_rsrc(const char* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Per-chunk description, uniform: where the chunk's keys start, and what the
+// mask needs.
+struct ChunkMeta {
+  int tok0;       // first key token of the chunk
+  int limit;      // dense chunks: end of the chunk's token range
+  unsigned flag;  // tile-map flags (0 for dense chunks)
+  int ky0, kx0;   // key-tile origin (image chunks)
+};
+
+__device__ __forceinline__ ChunkMeta chunk_meta(const KeySource& ks, int j) {
+  ChunkMeta m;
+  if (j < ks.n_dense) {
+    const bool first = j < ks.n_dense1;
+    m.tok0 = first ? ks.dense_base + j * kChunk : ks.dense2_base + (j - ks.n_dense1) * kChunk;
+    m.limit = first ? ks.dense_limit : ks.dense2_limit;
+    m.flag = 0;
+    m.ky0 = 0;
+    m.kx0 = 0;
+  } else {
+    const int e = ks.e0 + j - ks.n_dense;
+    const uint32_t kt = ks.key_tiles[e];
+    m.flag = (ks.flags32[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+    const int kty = (int)(((uint64_t)kt * ks.nkx_magic) >> 32);
+    m.ky0 = kty * kKeyH;
+    m.kx0 = ((int)kt - kty * ks.nkx) * kKeyW;
+    m.tok0 = ks.n_text + m.ky0 * ks.gw + m.kx0;
+    m.limit = 0;
+  }
+  return m;
+}
+
+// Offset of a padding slot: past any buffer bound, so its load returns zeros.
+constexpr uint32_t kNoPiece = 0xfffffff0u;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// What one wavefront does with chunk j: whether it computes it at all, and
+// which mask applies (tail of a dense range, or the circular window).
+struct ChunkInfo {
+  bool active;
+  bool coord;
+  bool square;  // square-window variant
+  bool inside;  // key tile wholly on the grid
+  int tail;     // dense chunk: positions >= tail are masked
+  int ky0, kx0;
+};
+
+__device__ __forceinline__ ChunkInfo chunk_info(const ChunkMeta& m, int j, const KeySource& ks, int wave) {
+  ChunkInfo c{true, false, false, true, 32, m.ky0, m.kx0};
+  c.square = ks.window == 1;
+  if (j < ks.n_dense) {
+    const int rem = m.limit - m.tok0;
+    c.tail = rem < 32 ? rem : 32;
+  } else {
+    c.active = (m.flag >> wave) & 1u;
+    c.coord = !((m.flag >> (8 + wave)) & 1u);
+    c.inside = m.ky0 + kKeyH <= ks.gh && m.kx0 + kKeyW <= ks.gw;
+  }
+  return c;
+}
+
+
+// The window mask of one chunk, in place on 32x32 accumulator values s whose
+// rows are the chunk's 32 positions (register i of lane group g is position
+// acc_row(i, g)) and whose column is the lane's own cell (cy, cx).  A dense
+// chunk masks positions >= tail; a key-tile chunk that is not wholly admitted
+// masks by coordinates: position 8a + c is cell (ky0 + a, kx0 + c), admitted
+// iff dx^2 <= lim[a], lim = r2 - dy^2 (circle) or lim = dy^2 <= r2 ? r2 : -1
+// (square), with the chunk's cell on the grid.  The distance is symmetric, so
+// the same code serves a query column against key rows and a key column
+// against query rows.
+__device__ __forceinline__ void mask_chunk(f32x16_t& s, const ChunkInfo& c, const KeySource& ks, int g,
+                                           int cy, int cx, int r2) {
+  if (c.tail < 32) {
+    for (int i = 0; i < 16; ++i) s[i] = acc_row(i, g) >= c.tail ? -__builtin_inff() : s[i];
+  } else if (c.coord) {
+    int lim[4], dxx[4];
+    const int dy0 = cy - c.ky0, dx0 = cx - c.kx0 - 4 * g;
+    if (c.square) {
+      for (int a = 0; a < 4; ++a) lim[a] = __mul24(dy0 - a, dy0 - a) <= r2 ? r2 : -1;
+    } else {
+      for (int a = 0; a < 4; ++a) lim[a] = r2 - __mul24(dy0 - a, dy0 - a);
+    }
+    for (int b = 0; b < 4; ++b) dxx[b] = __mul24(dx0 - b, dx0 - b);
+    if (!c.inside) {
+      for (int a = 0; a < 4; ++a)
+        if (c.ky0 + a >= ks.gh) lim[a] = -1;
+      for (int b = 0; b < 4; ++b)
+        if (c.kx0 + 4 * g + b >= ks.gw) dxx[b] = 0x7fffffff;
+    }
+    for (int i = 0; i < 16; ++i) s[i] = dxx[i & 3] > lim[i >> 2] ? -__builtin_inff() : s[i];
+  }
+}
+
+}  // namespace
+}  // namespace clear

@@ -26,52 +26,24 @@
 // V^T read from row-major V by the LDS transpose load ds_read_b64_tr_b16; fp32
 // uses v_mfma_f32_32x32x2_f32.
 //
-// Pipeline: three LDS stages and two register sets.  Chunk c is fetched from
-// global memory into register set c % 2 three iterations before it is
-// consumed, written to LDS stage c % 3 one iteration before, and its Q.K
-// products are issued one iteration early (overlapping the previous chunk's
-// softmax); one workgroup barrier per chunk.
+// Pipeline: two LDS stages and one workgroup barrier per chunk.  Each chunk
+// goes from global memory straight into LDS (direct-to-LDS buffer loads issued
+// by all four wavefronts) one iteration before it is consumed, so the copy of
+// chunk j + 1 overlaps the computation on chunk j.  Three wavefronts per SIMD
+// (bf16) hide the remaining latency.
 //
 // Online softmax in base 2 with a lazily updated reference max: p = 2^(s*c - M)
 // with c = log2(e)/sqrt(d); M is raised only when a row max exceeds M + 8, so
 // p <= 256 and O / L is unchanged (softmax is invariant to the reference).
-#include <hip/hip_runtime.h>
-
-#include "clear_internal.h"
+#include "attn_common.h"
 
 namespace clear {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-typedef __attribute__((ext_vector_type(2))) float f32x2_t;
-typedef __attribute__((ext_vector_type(16))) float f32x16_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
-typedef __attribute__((ext_vector_type(2))) short s16x2_t;
-typedef __attribute__((ext_vector_type(4))) short s16x4_t;
-typedef __attribute__((ext_vector_type(8))) short s16x8_t;
-typedef __attribute__((address_space(3))) char lds_char_t;
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int kTileH = CLEAR_TILE_H;
-constexpr int kTileW = CLEAR_TILE_W;
-constexpr int kSubH = CLEAR_SUB_H;
-constexpr int kChunk = CLEAR_CHUNK;
 constexpr int kStages = 2;
-constexpr int kKeyH = CLEAR_KEY_H;
-constexpr int kKeyW = CLEAR_KEY_W;
 constexpr int kTextQ = kWaves * 32;  // text queries per workgroup
 constexpr float kLazyTau = 8.0f;
 constexpr float kMInit = -1.0e30f;
-
-static_assert(kTileH == kWaves * kSubH && kTileW == CLEAR_SUB_W && kTileW * kSubH == 32,
-              "one 32-query sub-tile per wavefront");
-static_assert(kChunk == 32, "chunk = one 32-row MFMA block");
-static_assert(kKeyH * kKeyW == kChunk && kKeyW == 8,
-              "key tile = one chunk; key cell (a, c) is chunk position 8a + c");
 
 struct Params {
   const char* q;
@@ -98,20 +70,6 @@ struct Params {
   int partial_out;  // text workgroups write unnormalised partials (O, M, L)
   float scale_log2;
 };
-
-// Key position m (0..31) of accumulator register i in lane group g: the row
-// index of the 32x32 accumulator layout.
-__device__ __forceinline__ int acc_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
-
-// Wave-wide combine of a value with its partner lane l ^ 32.
-__device__ __forceinline__ float max_xor32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_xor32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // ---------------------------------------------------------------- engines
 
@@ -296,66 +254,6 @@ struct F32 {
   }
 };
 
-// ---------------------------------------------------------------- key sources
-
-// Maps (chunk j, position p) to a key token for the current workgroup.
-// Chunks 0 .. n_dense-1 come from one or two dense token ranges (the text keys
-// of an image tile; a key range of a text workgroup; or the text keys and one
-// strip's image rows); chunk n_dense + e is the e-th key
-// tile the tile map lists for the query tile, position p = 8a + c being its
-// key cell (ky0 + a, kx0 + c).
-typedef __attribute__((address_space(4))) const uint32_t const_u32_t;
-
-struct KeySource {
-  // dense chunks 0 .. n_dense1-1 cover tokens [dense_base, dense_limit), chunks
-  // n_dense1 .. n_dense-1 cover [dense2_base, dense2_limit)
-  int dense_base, dense_limit, n_dense1, dense2_base, dense2_limit, n_dense;
-  int n_text, gh, gw, nkx;
-  uint64_t nkx_magic;    // ceil(2^32 / nkx): kt / nkx == (kt * magic) >> 32 here
-  int e0;                // the query tile's first tile-map entry
-  int window;            // 0 circle, 1 square
-  int n_tok;             // tokens per head (N)
-  const_u32_t* key_tiles;  // whole tile map, read through the scalar cache
-  const_u32_t* flags32;    // u16 flags, two per word
-};
-
-// Buffer resource over `bytes` bytes from a uniform address (gfx9 resource
-// word 3).  Loads at offsets >= bytes return zero instead of touching memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_rsrc(const char* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// Per-chunk description, uniform: where the chunk's keys start, and what the
-// mask needs.
-struct ChunkMeta {
-  int tok0;       // first key token of the chunk
-  int limit;      // dense chunks: end of the chunk's token range
-  unsigned flag;  // tile-map flags (0 for dense chunks)
-  int ky0, kx0;   // key-tile origin (image chunks)
-};
-
-__device__ __forceinline__ ChunkMeta chunk_meta(const KeySource& ks, int j) {
-  ChunkMeta m;
-  if (j < ks.n_dense) {
-    const bool first = j < ks.n_dense1;
-    m.tok0 = first ? ks.dense_base + j * kChunk : ks.dense2_base + (j - ks.n_dense1) * kChunk;
-    m.limit = first ? ks.dense_limit : ks.dense2_limit;
-    m.flag = 0;
-    m.ky0 = 0;
-    m.kx0 = 0;
-  } else {
-    const int e = ks.e0 + j - ks.n_dense;
-    const uint32_t kt = ks.key_tiles[e];
-    m.flag = (ks.flags32[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-    const int kty = (int)(((uint64_t)kt * ks.nkx_magic) >> 32);
-    m.ky0 = kty * kKeyH;
-    m.kx0 = ((int)kt - kty * ks.nkx) * kKeyW;
-    m.tok0 = ks.n_text + m.ky0 * ks.gw + m.kx0;
-    m.limit = 0;
-  }
-  return m;
-}
-
 // Staging a chunk into LDS with direct-to-LDS buffer loads.  One load
 // instruction of a wavefront fills one 1 KB block (lane l writes 16-byte slot
 // 64 * block + l); the K region holds key rows at a pitch of kSlotsK slots, the
@@ -373,7 +271,6 @@ struct DmaPlan {
   uint32_t dense_v[kPerWaveV], tile_v[kPerWaveV];
 };
 
-constexpr uint32_t kNoPiece = 0xfffffff0u;
 
 template <class E>
 __device__ __forceinline__ void slot_offsets(int slot, int slots_per_row, int gw, uint32_t& dense,
@@ -397,7 +294,6 @@ __device__ __forceinline__ DmaPlan<E> make_plan(int wave, int lane, int gw) {
   return pl;
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 template <class E>
 __device__ __forceinline__ void dma_blocks(char* st, int wave, __amdgpu_buffer_rsrc_t rk,
@@ -436,35 +332,6 @@ struct SoftmaxState {
   float M, L;
 };
 
-// What one wavefront does with chunk j: whether it computes it at all, and
-// which mask applies (tail of a dense range, or the circular window).
-struct ChunkInfo {
-  bool active;
-  bool coord;
-  bool square;  // square-window variant
-  bool inside;  // key tile wholly on the grid
-  int tail;     // dense chunk: positions >= tail are masked
-  int ky0, kx0;
-};
-
-__device__ __forceinline__ ChunkInfo chunk_info(const ChunkMeta& m, int j, const KeySource& ks, int wave) {
-  ChunkInfo c{true, false, false, true, 32, m.ky0, m.kx0};
-  c.square = ks.window == 1;
-  if (j < ks.n_dense) {
-    const int rem = m.limit - m.tok0;
-    c.tail = rem < 32 ? rem : 32;
-  } else {
-    c.active = (m.flag >> wave) & 1u;
-    c.coord = !((m.flag >> (8 + wave)) & 1u);
-    c.inside = m.ky0 + kKeyH <= ks.gh && m.kx0 + kKeyW <= ks.gw;
-  }
-  return c;
-}
-
-enum MaskMode { kMaskNone = 0, kMaskTail = 1, kMaskCoord = 2 };
-
-// Mask, online softmax and P.V for the logits s of one chunk (one wavefront).
-// One straight-line instance per mask mode, so the logits are masked in place.
 // Logits of one chunk -> masked, online-softmax probabilities (base 2, lazy
 // reference max).  Returns the factor O must be scaled by before this chunk's
 // P.V (1 unless the reference max moved); O itself is not touched here, so the
@@ -473,29 +340,7 @@ template <class E>
 __device__ __forceinline__ float chunk_probs(SoftmaxState& sm, f32x16_t& s, const ChunkInfo& c,
                                              const KeySource& ks, int lane, int qy, int qx, int r2,
                                              float scale_log2, typename E::Probs& pr) {
-  const int g = lane >> 5;
-  if (c.tail < 32) {
-    for (int i = 0; i < 16; ++i) s[i] = acc_row(i, g) >= c.tail ? -__builtin_inff() : s[i];
-  } else if (c.coord) {
-    // Register i of lane group g holds key cell (ky0 + i/4, kx0 + 4g + i%4) of
-    // the key tile; admitted iff dx^2 <= lim, lim = r2 - dy^2 (circle) or
-    // lim = dy^2 <= r2 ? r2 : -1 (square), with both cells on the grid.
-    int lim[4], dxx[4];
-    const int dy0 = qy - c.ky0, dx0 = qx - c.kx0 - 4 * g;
-    if (c.square) {
-      for (int a = 0; a < 4; ++a) lim[a] = __mul24(dy0 - a, dy0 - a) <= r2 ? r2 : -1;
-    } else {
-      for (int a = 0; a < 4; ++a) lim[a] = r2 - __mul24(dy0 - a, dy0 - a);
-    }
-    for (int b = 0; b < 4; ++b) dxx[b] = __mul24(dx0 - b, dx0 - b);
-    if (!c.inside) {
-      for (int a = 0; a < 4; ++a)
-        if (c.ky0 + a >= ks.gh) lim[a] = -1;
-      for (int b = 0; b < 4; ++b)
-        if (c.kx0 + 4 * g + b >= ks.gw) dxx[b] = 0x7fffffff;
-    }
-    for (int i = 0; i < 16; ++i) s[i] = dxx[i & 3] > lim[i >> 2] ? -__builtin_inff() : s[i];
-  }
+  mask_chunk(s, c, ks, lane >> 5, qy, qx, r2);
   float mx = s[0];
   for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
   mx = max_xor32(mx);

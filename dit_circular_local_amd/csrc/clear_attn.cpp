@@ -83,7 +83,8 @@ int get_tile_map(DevState& ds, int gh, int gw, int r2, int window, hipStream_t s
 
 // Text-row split count: make a text workgroup's key range (its critical path)
 // at most about half of the ideal time of the whole launch.
-int choose_text_splits(int B, int H, int n_text, int N, int ntiles, size_t img_chunks) {
+int choose_text_splits(int B, int H, int n_text, int N, int ntiles, size_t img_chunks,
+                       double waves_per_simd = 3.0) {
   // img_chunks: listed key tiles (32 keys each) over all query tiles
   if (n_text == 0) return 1;
   const double nall = (N + CLEAR_CHUNK - 1) / CLEAR_CHUNK;
@@ -92,7 +93,7 @@ int choose_text_splits(int B, int H, int n_text, int N, int ntiles, size_t img_c
   // wavefront-chunks of work (each = 32 queries x 32 keys)
   const double w_img = (double)B * H * (4.0 * ntiles * nt_ch + 3.0 * (double)img_chunks);
   const double w_text = (double)B * H * text_blocks * 4.0 * nall;
-  const double slots = 256.0 * 4.0 * 3.0;  // CUs x SIMDs x resident waves
+  const double slots = 256.0 * 4.0 * waves_per_simd;  // CUs x SIMDs x resident waves
   const double t_ideal = (w_img + w_text) / slots;
   int s = (int)(2.0 * nall / (t_ideal > 1.0 ? t_ideal : 1.0)) + 1;
   int smax = (int)(nall / 8.0);
@@ -100,6 +101,25 @@ int choose_text_splits(int B, int H, int n_text, int N, int ntiles, size_t img_c
   if (s > 64) s = 64;
   if (s < 1) s = 1;
   return s;
+}
+
+// Grow the device's library workspace to at least `need` bytes.  Caller holds g_mu.
+int workspace(DevState& ds, size_t need, void** out) {
+  if (need > ds.ws_bytes) {
+    hipError_t e;
+    // the old workspace may still be read by queued kernels
+    if (ds.ws) {
+      if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+      (void)hipFree(ds.ws);
+      ds.ws = nullptr;
+      ds.ws_bytes = 0;
+    }
+    if ((e = hipMalloc(&ds.ws, need)) != hipSuccess)
+      return set_error(CLEAR_ENOMEM, "workspace (%zu bytes): %s", need, hipGetErrorString(e));
+    ds.ws_bytes = need;
+  }
+  *out = ds.ws;
+  return CLEAR_OK;
 }
 
 bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -134,7 +154,7 @@ using namespace clear;
 
 extern "C" const char* clear_last_error(void) { return g_err; }
 
-extern "C" int clear_version(void) { return 10200; }
+extern "C" int clear_version(void) { return 10300; }
 
 namespace {
 
@@ -221,20 +241,10 @@ int run_forward(const void* q, const void* k, const void* v, void* out, int B, i
   } else if (splits > 1 && n_text > 0) {
     const size_t o_bytes = align_up((size_t)splits * B * H * n_text * d * 4, 256);
     const size_t need = o_bytes + (size_t)splits * B * H * n_text * 2 * 4;
-    if (need > ds.ws_bytes) {
-      // the old workspace may still be read by queued kernels
-      if (ds.ws) {
-        if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-        (void)hipFree(ds.ws);
-        ds.ws = nullptr;
-        ds.ws_bytes = 0;
-      }
-      if ((e = hipMalloc(&ds.ws, need)) != hipSuccess)
-        return set_error(CLEAR_ENOMEM, "text workspace (%zu bytes): %s", need, hipGetErrorString(e));
-      ds.ws_bytes = need;
-    }
-    a.ws_o = (float*)ds.ws;
-    a.ws_ml = (float*)((char*)ds.ws + o_bytes);
+    void* ws = nullptr;
+    if ((rc = workspace(ds, need, &ws)) != CLEAR_OK) return rc;
+    a.ws_o = (float*)ws;
+    a.ws_ml = (float*)((char*)ws + o_bytes);
   }
   rc = attn_launch(a, stream);
   if (rc) return rc;
@@ -245,7 +255,102 @@ int run_forward(const void* q, const void* k, const void* v, void* out, int B, i
   return CLEAR_OK;
 }
 
+int run_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int H, int d, int n_text,
+                 int grid_h, int grid_w, const clear_opts* opts, void* stream) {
+  clear_opts o = opts ? *opts : clear_opts{CLEAR_BF16, 0, nullptr, 0, CLEAR_WINDOW_CIRCLE};
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
+    return set_error(CLEAR_EINVAL, "q, k, v, out, dout, lse, dq, dk and dv must not be NULL");
+  if (B < 1 || H < 1) return set_error(CLEAR_EINVAL, "B and H must be >= 1 (got %d, %d)", B, H);
+  if (d != 64 && d != 128) return set_error(CLEAR_EINVAL, "d must be 64 or 128 (got %d)", d);
+  if (n_text < 0) return set_error(CLEAR_EINVAL, "n_text must be >= 0 (got %d)", n_text);
+  if (grid_h < 1 || grid_w < 1 || grid_h > CLEAR_MAX_GRID || grid_w > CLEAR_MAX_GRID)
+    return set_error(CLEAR_EINVAL, "grid sides must be in 1..%d (got %d x %d)", CLEAR_MAX_GRID, grid_h, grid_w);
+  if (o.dtype != CLEAR_BF16 && o.dtype != CLEAR_FP32)
+    return set_error(CLEAR_EINVAL, "dtype must be CLEAR_BF16 or CLEAR_FP32 (got %d)", o.dtype);
+  if (o.r2_max < -1) return set_error(CLEAR_EINVAL, "r2_max must be >= -1 (got %d)", o.r2_max);
+  if (o.window != CLEAR_WINDOW_CIRCLE && o.window != CLEAR_WINDOW_SQUARE)
+    return set_error(CLEAR_EINVAL, "window must be CLEAR_WINDOW_CIRCLE or CLEAR_WINDOW_SQUARE (got %d)",
+                     o.window);
+  if (n_text == 0 && o.r2_max < 0)
+    return set_error(CLEAR_EINVAL, "n_text == 0 and r2_max < 0: every query row would be empty");
+  if (o.text_splits < 0 || o.text_splits > 64)
+    return set_error(CLEAR_EINVAL, "text_splits must be in 0..64 (got %d)", o.text_splits);
+  if (o.lse_out) return set_error(CLEAR_EINVAL, "lse_out is a forward output; pass NULL to the backward");
+  const long long N = (long long)n_text + (long long)grid_h * grid_w;
+  if (N > 0x7fffffffLL) return set_error(CLEAR_EINVAL, "sequence too long");
+  const size_t elem = o.dtype == CLEAR_BF16 ? 2 : 4;
+  const size_t bytes = (size_t)B * H * (size_t)N * d * elem;
+  const size_t lse_bytes = (size_t)B * H * (size_t)N * 4;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)dout | (uintptr_t)dq |
+       (uintptr_t)dk | (uintptr_t)dv) & 15)
+    return set_error(CLEAR_EINVAL, "q, k, v, out, dout, dq, dk and dv must be 16-byte aligned");
+  if ((uintptr_t)lse & 3) return set_error(CLEAR_EINVAL, "lse must be 4-byte aligned");
+  const void* ins[5] = {q, k, v, out, dout};
+  void* grads[3] = {dq, dk, dv};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 5; ++j)
+      if (ranges_overlap(grads[i], bytes, ins[j], bytes))
+        return set_error(CLEAR_EINVAL, "dq, dk and dv must not overlap q, k, v, out or dout");
+    if (ranges_overlap(grads[i], bytes, lse, lse_bytes))
+      return set_error(CLEAR_EINVAL, "dq, dk and dv must not overlap lse");
+    for (int j = i + 1; j < 3; ++j)
+      if (ranges_overlap(grads[i], bytes, grads[j], bytes))
+        return set_error(CLEAR_EINVAL, "dq, dk and dv must not overlap each other");
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+
+  std::lock_guard<std::mutex> lock(g_mu);
+  DevState& ds = g_dev[dev];
+  TileMapDev* tm = nullptr;
+  int rc = get_tile_map(ds, grid_h, grid_w, o.r2_max, o.window, s, &tm);
+  if (rc) return rc;
+  if ((e = hipStreamWaitEvent(s, tm->ready, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+
+  TileGeom g = make_geom(grid_h, grid_w, o.r2_max, CLEAR_TILE_H, CLEAR_TILE_W, CLEAR_SUB_H, CLEAR_SUB_W,
+                         CLEAR_KEY_H, CLEAR_KEY_W, o.window);
+  const int splits = o.text_splits ? o.text_splits
+                                   : choose_text_splits(B, H, n_text, (int)N, g.nty * g.ntx, tm->n_entries, 2.0);
+  const size_t stats_bytes = align_up((size_t)B * H * (size_t)N * 8, 256);
+  const size_t part_bytes = n_text > 0 ? align_up((size_t)splits * B * H * n_text * d * 4, 256) : 0;
+  void* ws = nullptr;
+  if ((rc = workspace(ds, stats_bytes + 3 * part_bytes, &ws)) != CLEAR_OK) return rc;
+
+  BwdLaunch a;
+  memset(&a, 0, sizeof a);
+  a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.ws_stats = (float*)ws;
+  if (n_text > 0) {
+    a.ws_dq = (float*)((char*)ws + stats_bytes);
+    a.ws_dk = (float*)((char*)ws + stats_bytes + part_bytes);
+    a.ws_dv = (float*)((char*)ws + stats_bytes + 2 * part_bytes);
+  }
+  a.tm_offsets = tm->offsets; a.tm_key_tiles = tm->key_tiles; a.tm_flags = tm->flags;
+  a.B = B; a.H = H; a.d = d; a.n_text = n_text; a.gh = grid_h; a.gw = grid_w; a.r2 = g.r2;
+  a.dtype = o.dtype; a.text_splits = splits; a.window = o.window;
+  rc = attn_bwd_launch(a, stream);
+  if (rc) return rc;
+  if (debug_sync_enabled()) {
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "CLEAR_DEBUG sync");
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "CLEAR_DEBUG check");
+  }
+  return CLEAR_OK;
+}
+
 }  // namespace
+
+extern "C" int clear_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                              const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                              int H, int d, int n_text, int grid_h, int grid_w, const clear_opts* opts,
+                              void* stream) {
+  clear_error_reset();
+  return run_backward(q, k, v, out, dout, lse, dq, dk, dv, B, H, d, n_text, grid_h, grid_w, opts, stream);
+}
 
 extern "C" int clear_attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B,
                                  int H, int d, int n_text, int grid_h, int grid_w,

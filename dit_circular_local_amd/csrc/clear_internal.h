@@ -46,6 +46,32 @@ struct AttnLaunch {
 };
 
 int attn_launch(const AttnLaunch& a, void* stream);
+
+// Backward launch description (all pointers are device pointers).
+struct BwdLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;    // forward output O
+  const void* dout;   // upstream gradient dO
+  const float* lse;   // forward LSE [B*H][N], natural log
+  void* dq;
+  void* dk;
+  void* dv;
+  float* ws_stats;    // [B*H][N][2]: (lse * log2(e), dO . O)
+  float* ws_dq;       // text partials [splits][B*H][n_text][d]   (n_text > 0)
+  float* ws_dk;
+  float* ws_dv;
+  const uint32_t* tm_offsets;
+  const uint32_t* tm_key_tiles;
+  const uint16_t* tm_flags;
+  int B, H, d, n_text, gh, gw, r2;
+  int dtype;
+  int text_splits;
+  int window;
+};
+
+int attn_bwd_launch(const BwdLaunch& a, void* stream);
 int text_merge_launch(const float* part_o, const float* part_ml, int nparts, int mode, void* out,
                       float* lse, int BH, int n_text, int N, int d, int dtype, void* stream);
 

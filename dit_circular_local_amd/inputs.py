@@ -22,6 +22,10 @@ with round-to-nearest-even.
 Every (tensor, batch, head) slab has its own seed derived from the base seed,
 so any head can be regenerated alone (the oracle checks sampled heads of the
 512x512 workload without drawing all 24).
+
+The backward's upstream gradient dO is drawn the same way (N(0, 1) times the
+workload's scale, rounded to its dtype, no normalisation), from seeds of its
+own.
 """
 
 from __future__ import annotations
@@ -31,7 +35,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_qkv", "make_head", "slab_seed"]
+__all__ = ["Workload", "WORKLOADS", "make_qkv", "make_head", "make_dout", "slab_seed"]
 
 
 @dataclass(frozen=True)
@@ -64,8 +68,14 @@ WORKLOADS = {
 _TENSOR_ID = {"q": 0, "k": 1, "v": 2}
 
 
+_DOUT_BASE = 1 << 48
+
+
 def slab_seed(seed: int, tensor: str, b: int, h: int) -> int:
-    """Seed of one [N, d] slab: a fixed injective map of (seed, tensor, b, h)."""
+    """Seed of one [N, d] slab: a fixed injective map of (seed, tensor, b, h);
+    tensor "dout" maps above every Q/K/V seed."""
+    if tensor == "dout":
+        return _DOUT_BASE + slab_seed(seed, "q", b, h)
     return ((seed * 3 + _TENSOR_ID[tensor]) * 4096 + b) * 4096 + h
 
 
@@ -107,6 +117,18 @@ def make_qkv(B: int, H: int, n_text: int, grid_h: int, grid_w: int, d: int,
                 t[b, h].copy_(make_head(n, d, name, b, h, seed, dtype, rms_norm, scale, q_mult))
         out.append(t)
     return tuple(out)
+
+
+def make_dout(B: int, H: int, n: int, d: int, dtype: str = "bf16", seed: int = 0,
+              scale: float = 1.0, device: Optional[str] = None) -> torch.Tensor:
+    """Upstream gradient dO [B, H, n, d]: N(0, 1) * scale per slab, rounded to dtype."""
+    t = torch.empty((B, H, n, d), dtype=_torch_dtype(dtype), device=device or "cpu")
+    for b in range(B):
+        for h in range(H):
+            g = torch.Generator(device="cpu")
+            g.manual_seed(slab_seed(seed, "dout", b, h))
+            t[b, h].copy_((torch.randn(n, d, generator=g, dtype=torch.float32) * scale).to(t.dtype))
+    return t
 
 
 def workload_qkv(w: Workload, seed: int = 0, device: Optional[str] = None,

@@ -1,6 +1,6 @@
 /*
  * clear_attn.h -- C ABI of libclear_attn.so: the forward pass of CLEAR
- * circular-window attention on AMD Instinct MI355X (gfx950).
+ * circular-window attention on AMD Instinct MI355X (gfx950), and its gradients.
  *
  * The operation (CLEAR, arXiv 2412.16112; mask as written in the pith.science
  * review of the paper, section "Core claim"; softmax attention with 1/sqrt(c)
@@ -36,7 +36,11 @@
  *     CLEAR_EHIP).
  *   - Faults inside kernels surface at the caller's next synchronisation.
  *   - Thread safety: every entry point may be called from several host
- *     threads; the library's caches are guarded by a mutex.
+ *     threads; the library's caches are guarded by a mutex.  Calls that use
+ *     the library's workspace (the text-row partials of clear_attn_fwd* and
+ *     the statistics and partials of clear_attn_bwd) share one buffer per
+ *     device: calls on one stream are ordered and safe; calls running
+ *     concurrently on different streams of one device race on it.
  */
 #ifndef CLEAR_ATTN_H
 #define CLEAR_ATTN_H
@@ -171,6 +175,40 @@ int clear_attn_fwd_strip(const void* q, const void* k, const void* v, void* out,
 int clear_text_merge(const float* part_o, const float* part_ml, int nparts, int mode,
                      void* out, float* lse_out, int B, int H, int d, int n_text,
                      int grid_h, int grid_w, int dtype, void* stream);
+
+/*
+ * clear_attn_bwd -- gradients of one CLEAR attention layer (added in 1.3).
+ * The backward is the step that follows the forward in the paper's
+ * attention-only distillation fine-tuning (pith.science review of arXiv
+ * 2412.16112, "What carries the argument").  For the forward
+ * O = softmax_M(Q K^T / sqrt(d)) V and an upstream gradient dO = dL/dO:
+ *
+ *   P_ij  = M_ij exp(s_ij - lse_i),  s_ij = q_i . k_j / sqrt(d)
+ *   dV_j  = sum_i P_ij dO_i
+ *   dS_ij = P_ij (dO_i . v_j - dO_i . O_i)
+ *   dQ_i  = sum_j dS_ij k_j / sqrt(d),   dK_j = sum_i dS_ij q_i / sqrt(d)
+ *
+ *   q, k, v   : device, [B, H, N, d] contiguous, the forward's inputs.
+ *   out       : device, [B, H, N, d], the forward's output O (same call options).
+ *   dout      : device, [B, H, N, d], the upstream gradient dO.
+ *   lse       : device, [B, H, N] float32, the forward's lse_out (natural log).
+ *   dq, dk, dv: device, [B, H, N, d] contiguous outputs, every element written;
+ *               must not overlap each other or any input.
+ *   All of q .. dv are caller-owned, of opts->dtype, 16-byte aligned (lse:
+ *   4-byte aligned).  Shapes, dtype, r2_max, window and their checks as
+ *   clear_attn_fwd_ex; opts->lse_out must be NULL; opts->text_splits sets how
+ *   many query (key) ranges the text keys' (text queries') gradient rows are
+ *   split into (0 = chosen by the library), summed in a final step.
+ * Arithmetic (bf16): bf16 inputs, fp32 accumulation, P and dS rounded to bf16
+ * for the matrix-core products, D = dO . O in fp32, outputs rounded to bf16.
+ * The library owns a workspace of B*H*N*8 bytes of row statistics plus
+ * 3 * splits * B*H*n_text*d*4 bytes of text-row partials (see the thread
+ * safety note above).
+ */
+int clear_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   int B, int H, int d, int n_text, int grid_h, int grid_w,
+                   const clear_opts* opts, void* stream);
 
 /*
  * clear_tile_map_size -- number of entries of the tile map (host, closed form).

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert ca.version() == 10200  # 1.2.0: strips and text-row merging
+    assert ca.version() == 10300  # 1.3.0: gradients (clear_attn_bwd)
 
 
 # fake, aligned, non-overlapping device addresses: validation must fail before use

@@ -1,0 +1,170 @@
+"""GPU parity of the backward (clear_attn_bwd) against the fp64 oracle's
+gradients, through the C ABI.
+
+The GPU backward takes the GPU forward's output and LSE, as a training step
+does; the oracle differentiates its own forward.  Bars:
+
+* fp32: max-abs 1e-5 on every element (this also pins the masks: a pair
+  missing from the mask moves a gradient by orders of magnitude more);
+* bf16: the error of each gradient tensor of a head, relative to its largest
+  entry, at most 2^-6.  Derivation: every gradient entry is a sum of products
+  in which the GPU rounds one factor to bf16 (P for dV, dS for dK and dQ;
+  relative error 2^-9 each) and rounds the result to bf16 (2^-9); the forward
+  output O it reads for D = dO . O carries the forward's own bf16 error.  The
+  summed rounding errors stay below a few units of 2^-9 of the largest entry
+  (at most 3.1 x 2^-9 measured over the cases here); 2^-6 = 8 x 2^-9 leaves a
+  margin of 2.5x and stays far below what a wrong index or sign produces
+  (order 1).
+* tile walks and split counts never change results beyond these bars, and two
+  runs are bit-identical (no atomics).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import dit_circular_local_amd as ca
+from dit_circular_local_amd.inputs import WORKLOADS, make_dout, make_qkv, workload_qkv
+from oracle import attention_backward, attention_backward_head, key_grads
+
+pytestmark = pytest.mark.gpu
+
+FP32_TOL = 1e-5
+BF16_REL = 2.0 ** -6
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _inputs(dtype, B, H, n_text, gh, gw, d, seed, q_mult=1.0):
+    scale = 1.0 if dtype == "bf16" else 1.0 / math.sqrt(d)
+    q, k, v = make_qkv(B, H, n_text, gh, gw, d, dtype, seed, rms_norm=(dtype == "bf16"), scale=scale,
+                       q_mult=q_mult, device="cuda")
+    do = make_dout(B, H, n_text + gh * gw, d, dtype, seed, scale=1.0, device="cuda")
+    return q, k, v, do
+
+
+def _gpu_grads(q, k, v, do, n_text, gh, gw, r2, window="circle", text_splits=0):
+    out, lse = ca.fwd(q, k, v, n_text, gh, gw, r2=r2, return_lse=True, window=window)
+    grads = ca.bwd(q, k, v, out, do, lse, n_text, gh, gw, r2=r2, window=window, text_splits=text_splits)
+    torch.cuda.synchronize()
+    return grads
+
+
+def _compare(dtype, got, ref, label):
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        g = _np(g) if torch.is_tensor(g) else g
+        B, H = r.shape[:2]
+        for b in range(B):
+            for h in range(H):
+                err = np.abs(g[b, h] - r[b, h]).max()
+                scale = np.abs(r[b, h]).max()
+                if dtype == "fp32":
+                    assert err <= FP32_TOL, f"{label} {name}[{b},{h}]: max-abs {err:.3e} (scale {scale:.3e})"
+                else:
+                    assert err <= BF16_REL * scale, \
+                        f"{label} {name}[{b},{h}]: max-abs {err:.3e} = {err / scale:.2e} of scale {scale:.3e}"
+
+
+def _check(dtype, B, H, n_text, gh, gw, d, r2, seed=0, window="circle", text_splits=0, q_mult=1.0):
+    q, k, v, do = _inputs(dtype, B, H, n_text, gh, gw, d, seed, q_mult)
+    got = _gpu_grads(q, k, v, do, n_text, gh, gw, r2, window, text_splits)
+    ref = attention_backward(_np(q), _np(k), _np(v), _np(do), n_text, gh, gw, r2, workers=8, window=window)
+    _compare(dtype, got, ref, f"{dtype} {window} {gh}x{gw}+{n_text} d{d} r2={r2}")
+
+
+def test_tiny_fp32_every_element():
+    w = WORKLOADS["tiny"]
+    _check("fp32", w.B, w.H, w.n_text, w.grid_h, w.grid_w, w.d, 16)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n_text,gh,gw", [(8, 16, 16), (0, 19, 13), (130, 24, 40), (40, 4, 4)])
+@pytest.mark.parametrize("r2", [-1, 0, 1, 2, 9, 24, 64, 10 ** 6])
+def test_fp32_masks_exact(d, n_text, gh, gw, r2):
+    if n_text == 0 and r2 < 0:
+        pytest.skip("empty rows")
+    _check("fp32", 1, 2, n_text, gh, gw, d, r2)
+
+
+@pytest.mark.parametrize("r2", [0, 4, 25])
+@pytest.mark.parametrize("n_text,gh,gw", [(8, 16, 16), (33, 37, 19)])
+def test_fp32_square_window(n_text, gh, gw, r2):
+    _check("fp32", 1, 2, n_text, gh, gw, 128, r2, window="square")
+
+
+@pytest.mark.parametrize("n_text,gh,gw,r2", [(8, 16, 16, 4), (33, 37, 19, 16), (512, 20, 24, 64),
+                                             (130, 24, 40, 0), (0, 24, 24, 9)])
+def test_bf16_small_grids(n_text, gh, gw, r2):
+    _check("bf16", 1, 2, n_text, gh, gw, 128, r2, seed=1)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 64])
+def test_text_splits(splits):
+    _check("fp32", 1, 2, 100, 12, 20, 128, 16, seed=2, text_splits=splits)
+
+
+def test_batch_heads_and_peaked_softmax():
+    _check("fp32", 2, 3, 24, 10, 14, 64, 9, seed=3, q_mult=8.0)
+    _check("bf16", 2, 2, 24, 10, 14, 128, 9, seed=3, q_mult=4.0)
+
+
+@pytest.mark.parametrize("r", [8, 16])
+def test_flux_1024_heads(r):
+    """64x64 grid + 512 text, the 1024^2 FLUX shape, four heads."""
+    _check("bf16", 1, 4, 512, 64, 64, 128, r * r, seed=4)
+
+
+def test_deterministic():
+    q, k, v, do = _inputs("bf16", 1, 2, 64, 32, 32, 128, 5)
+    a = _gpu_grads(q, k, v, do, 64, 32, 32, 64)
+    b = _gpu_grads(q, k, v, do, 64, 32, 32, 64)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_flux_8192_sampled_rows():
+    """512x512 grid + 512 text, 24 heads, bf16, r = 32, as the bench times it:
+    dq of sampled query rows and dk, dv of sampled keys for two heads, against
+    the oracle's row- and key-restricted gradients."""
+    w = WORKLOADS["flux8k"]
+    q, k, v = workload_qkv(w, seed=0, device="cuda")
+    do = make_dout(w.B, w.H, w.n, w.d, "bf16", 0, device="cuda")
+    r2 = 32 * 32
+    out, lse = ca.fwd(q, k, v, w.n_text, w.grid_h, w.grid_w, r2=r2, return_lse=True)
+    dq, dk, dv = ca.bwd(q, k, v, out, do, lse, w.n_text, w.grid_h, w.grid_w, r2=r2)
+    torch.cuda.synchronize()
+    g = w.grid_h
+    blocks = [(0, 0), (31, 63), (63, 0), (30, 30)]   # 8x8 query blocks: corners, edge, centre
+    text_rows = [0, 255, w.n_text - 1]
+    # image keys only: a text key's gradient sums over every query of the head
+    # (checked against the whole oracle backward on the smaller grids)
+    keys = [w.n_text + 0, w.n_text + 250 * g + 251, w.n_text + g * g - 1]
+    for h in (0, 23):
+        qh, kh, vh, dh = (_np(t[0, h]) for t in (q, k, v, do))
+        ref_dq, _, _ = attention_backward_head(qh, kh, vh, dh, w.n_text, g, g, r2, text_rows=text_rows,
+                                               blocks=blocks)
+        rows = text_rows + [w.n_text + (8 * by + y) * g + 8 * bx + x for by, bx in blocks
+                            for y in range(8) for x in range(8)]
+        got = _np(dq[0, h, rows])
+        scale = np.abs(ref_dq[rows]).max()
+        assert np.abs(got - ref_dq[rows]).max() <= BF16_REL * scale, f"dq head {h}"
+        ref_dk, ref_dv = key_grads(qh, kh, vh, dh, w.n_text, g, g, r2, keys)
+        for name, gt, rf in (("dk", dk, ref_dk), ("dv", dv, ref_dv)):
+            err = np.abs(_np(gt[0, h, keys]) - rf).max()
+            assert err <= BF16_REL * np.abs(rf).max(), f"{name} head {h}: {err:.3e}"
+    del q, k, v, do, out, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+
+
+def test_bwd_rejects_bad_arguments():
+    q, k, v, do = _inputs("bf16", 1, 1, 8, 4, 4, 64, 6)
+    out, lse = ca.fwd(q, k, v, 8, 4, 4, radius=1, return_lse=True)
+    with pytest.raises(ValueError):
+        ca.bwd(q, k, v, out, do, lse[:, :, :-1], 8, 4, 4, radius=1)
+    with pytest.raises(ca.ClearError) as e:
+        ca.bwd(q, k, v, out, do, lse, 8, 4, 4, radius=1, grads=(q, torch.empty_like(q), torch.empty_like(q)))
+    assert e.value.code == ca.CLEAR_EINVAL and "overlap" in ca.last_error()

@@ -84,11 +84,17 @@ def computed_pairs(ca, n_text: int, gh: int, gw: int, r2: int, window: str = "ci
     return (0.5 * (qk + pv) + text_rows) * per_chunk
 
 
+# sources the forward attention kernel is compiled from (its traffic figures
+# hold only while these are unchanged)
+FWD_KERNEL_SOURCES = ("dit_circular_local_amd/csrc/attn_fwd.hip", "dit_circular_local_amd/csrc/attn_common.h",
+                      "dit_circular_local_amd/csrc/clear_internal.h", "dit_circular_local_amd/csrc/tile_geom.h",
+                      "include/clear_attn.h")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "dit_circular_local_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+    for name in FWD_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
@@ -143,7 +149,9 @@ def time_strips(ca, torch, q, k, v, w, radius, strips, steps, warmup):
     """The layer as `strips` horizontal strips (each one device's share in a
     patch-parallel run), run one after another on this GPU, then the text rows
     merged exactly and by the patch average (Eq. 7).  Returns per-strip and merge
-    times (HIP events on the launch stream)."""
+    times (HIP events on the launch stream; the timed passes give strip 0 the text
+    keys, as the exact merge needs) and the patch average's distance from the
+    exact text rows."""
     B, H, N, d = q.shape
     out = torch.empty_like(q)
     po = torch.empty((strips, B * H, w.n_text, d), dtype=torch.float32, device=q.device)
@@ -180,6 +188,16 @@ def time_strips(ca, torch, q, k, v, w, radius, strips, steps, warmup):
         times[it] = [a.elapsed_time(b) for a, b in ev]
     med = [sorted(t[i] for t in times)[steps // 2] for i in range(strips + 2)]
     halo_rows = math.isqrt(radius * radius)
+    # how far the patch average (Eq. 7: every patch holds the text keys) lands from
+    # the exact text rows
+    ca.text_merge(po, pml, out, w.n_text, w.grid_h, w.grid_w, mode="exact")
+    exact = out[:, :, :w.n_text].float().clone()
+    for s_, (y0, y1) in enumerate(rows):
+        ca.fwd_strip(q, k, v, w.n_text, w.grid_h, w.grid_w, y0, y1, out, po[s_], pml[s_],
+                     radius=radius, with_text_keys=True)
+    ca.text_merge(po, pml, out, w.n_text, w.grid_h, w.grid_w, mode="patch_average")
+    diff = (out[:, :, :w.n_text].float() - exact).abs()
+    torch.cuda.synchronize()
     return {
         "strips": strips,
         "rows_per_strip": w.grid_h // strips,
@@ -188,9 +206,37 @@ def time_strips(ca, torch, q, k, v, w, radius, strips, steps, warmup):
         "strips_ms_sum": round(sum(med[:strips]), 4),
         "merge_exact_ms": round(med[strips], 4),
         "merge_patch_average_ms": round(med[strips + 1], 4),
+        "eq7_vs_exact_text_rows": {"max_abs": round(float(diff.max()), 5),
+                                   "mean_abs": round(float(diff.mean()), 6),
+                                   "exact_rms": round(float(exact.pow(2).mean().sqrt()), 5)},
         "halo_rows_per_side": halo_rows,
         "halo_bytes_per_neighbour": halo_rows * w.grid_w * H * d * 2 * q.element_size(),
     }
+
+
+def time_backward(ca, torch, q, k, v, w, radius, steps, warmup):
+    """The layer's gradients (clear_attn_bwd) for a seeded upstream gradient,
+    given the forward's output and LSE (computed once, outside the timed
+    region).  Returns ms per call from HIP events on the launch stream."""
+    from dit_circular_local_amd.inputs import make_dout
+
+    do = make_dout(w.B, w.H, w.n, w.d, w.dtype, seed=0, device=q.device)
+    out, lse = ca.fwd(q, k, v, w.n_text, w.grid_h, w.grid_w, radius=radius, return_lse=True)
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    for _ in range(warmup):
+        ca.bwd(q, k, v, out, do, lse, w.n_text, w.grid_h, w.grid_w, radius=radius, grads=grads)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s_, e_ in ev:
+        s_.record(stream)
+        ca.bwd(q, k, v, out, do, lse, w.n_text, w.grid_h, w.grid_w, radius=radius, grads=grads)
+        e_.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(s_.elapsed_time(e_) for s_, e_ in ev)
+    del do, out, lse, grads
+    torch.cuda.empty_cache()
+    return ms[len(ms) // 2], sum(ms) / len(ms)
 
 
 def cpu_baseline(q, k, v, w, radius, budget_s):
@@ -247,6 +293,8 @@ def main():
                     help="also time the square-window variant at this radius (-1: none)")
     ap.add_argument("--strips", type=int, default=8,
                     help="also time the layer as this many horizontal strips plus text merges (0: none)")
+    ap.add_argument("--backward-radii", default="32,8",
+                    help="also time the backward (clear_attn_bwd) at these radii ('' : none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -369,6 +417,19 @@ def main():
         line[f"strips{args.strips}"] = st
         log(f"{args.strips} strips: max {st['strip_ms_max']:.3f} ms per strip, sum {st['strips_ms_sum']:.3f} ms, "
             f"merges {st['merge_exact_ms']:.3f} / {st['merge_patch_average_ms']:.3f} ms")
+    for r in [int(x) for x in args.backward_radii.split(",") if x.strip()]:
+        med, mean = time_backward(ca, torch, q, k, v, w, r, min(args.steps, 10), 2)
+        # the backward's algorithmic work: 5 products of 2d flops per admitted
+        # pair (S recomputed, dP, dV, dK, dQ) = 2.5x the forward's 4d
+        bflops = 2.5 * 4.0 * w.d * admitted_pairs(w.n_text, w.grid_h, w.grid_w, r * r) * w.B * w.H
+        line[f"backward_r{r}"] = {
+            "ms_per_layer": round(med, 4),
+            "ms_mean": round(mean, 4),
+            "in_window_tflops": round(bflops / (med * 1e-3) / 1e12, 3),
+            "pct_bf16_peak": round(100.0 * bflops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "flops_per_layer": bflops,
+        }
+        log(f"backward r={r}: {med:.3f} ms/layer, {line[f'backward_r{r}']['in_window_tflops']:.1f} TFLOP/s in-window")
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on a sample (~{args.cpu_seconds:.0f} s)...")
         line["cpu_baseline"] = cpu_baseline(q, k, v, w, main_r, args.cpu_seconds)

@@ -97,3 +97,28 @@ def test_python_binding_rejects_cpu_tensors():
         ca.fwd(q, q, q, 8, 4, 4, radius=2)
     with pytest.raises(ValueError):
         ca.fwd(q, q, q, 8, 4, 4)
+
+
+DO, LSE, DQ, DK, DV = 0x50000000, 0x60000000, 0x70000000, 0x80000000, 0x90000000
+
+
+def _bwd(dtype=0, r2=4, lse_out=None, splits=0, window=0, q=Q, k=K, v=V, o=O, do=DO, lse=LSE, dq=DQ,
+         dk=DK, dv=DV, **kw):
+    a = dict(ok)
+    a.update(kw)
+    opts = ca._Opts(dtype, r2, lse_out, splits, window)
+    return ca.lib().clear_attn_bwd(q, k, v, o, do, lse, dq, dk, dv, a["B"], a["H"], a["d"], a["n_text"],
+                                   a["gh"], a["gw"], ctypes.byref(opts), None)
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(d=96), "d must be"), (dict(B=0), "B and H"), (dict(gw=0), "grid sides"),
+    (dict(lse=0), "NULL"), (dict(dv=0), "NULL"), (dict(do=0), "NULL"),
+    (dict(dq=Q), "overlap"), (dict(dk=DQ + 4096), "overlap"), (dict(dv=LSE), "overlap"),
+    (dict(dq=DO - 16), "overlap"), (dict(lse=LSE + 2), "lse must be"), (dict(dk=DK + 8), "aligned"),
+    (dict(lse_out=0x1000), "lse_out"), (dict(splits=65), "text_splits"), (dict(window=3), "window"),
+    (dict(dtype=7), "dtype"), (dict(r2=-3), "r2_max"), (dict(n_text=0, r2=-1), "empty"),
+])
+def test_bwd_rejects_bad_arguments(kw, frag):
+    assert _bwd(**kw) == ca.CLEAR_EINVAL
+    assert frag in ca.last_error()

@@ -154,6 +154,41 @@ def _sample_rows(n_text, g, rng, n_img=48, n_txt=6):
     return sorted(set(rows))
 
 
+@pytest.mark.parametrize("r", [8, 16, 32])
+def test_flux_2048_whole_heads(r):
+    """128x128 grid + 512 text tokens, 24 heads in one launch (the 2048^2 FLUX
+    shape): three heads compared element by element with the oracle, every
+    output finite."""
+    w = WORKLOADS["flux2k"]
+    q, k, v = workload_qkv(w, seed=r, device="cuda")
+    out = ca.fwd(q, k, v, w.n_text, w.grid_h, w.grid_w, radius=r)
+    torch.cuda.synchronize()
+    heads = [0, 11, 23]
+    ref, _ = attention(_np(q[:, heads]), _np(k[:, heads]), _np(v[:, heads]), w.n_text, w.grid_h, w.grid_w,
+                       r * r, workers=8)
+    err = np.abs(_np(out[:, heads]) - ref).max()
+    assert err <= 2e-2, f"r={r}: max-abs {err:.3e}"
+    assert torch.isfinite(out).all()
+
+
+@pytest.mark.parametrize("r", [8, 16, 32])
+def test_flux_4096_sampled_rows(r):
+    """256x256 grid + 512 text tokens, 24 heads in one launch (the 4096^2
+    FLUX shape): sampled rows of two heads against the oracle row by row."""
+    w = WORKLOADS["flux4k"]
+    q, k, v = workload_qkv(w, seed=r, device="cuda")
+    out = ca.fwd(q, k, v, w.n_text, w.grid_h, w.grid_w, radius=r)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(100 + r)
+    for h in (0, 23):
+        rows = _sample_rows(w.n_text, w.grid_h, rng)
+        ref, _ = attention_rows(_np(q[0, h]), _np(k[0, h]), _np(v[0, h]), w.n_text, w.grid_h,
+                                w.grid_w, r * r, rows)
+        err = np.abs(_np(out[0, h, rows]) - ref).max()
+        assert err <= 2e-2, f"r={r} head {h}: max-abs {err:.3e}"
+    assert torch.isfinite(out).all()
+
+
 @pytest.mark.parametrize("r", [8, 32])
 def test_flux_8192_sampled_rows(r):
     """512x512 grid + 512 text tokens, 24 heads, bf16, the benchmark's launch

@@ -96,10 +96,11 @@ def test_fp32_square_window(n_text, gh, gw, r2):
     _check("fp32", 1, 2, n_text, gh, gw, 128, r2, window="square")
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("n_text,gh,gw,r2", [(8, 16, 16, 4), (33, 37, 19, 16), (512, 20, 24, 64),
                                              (130, 24, 40, 0), (0, 24, 24, 9)])
-def test_bf16_small_grids(n_text, gh, gw, r2):
-    _check("bf16", 1, 2, n_text, gh, gw, 128, r2, seed=1)
+def test_bf16_small_grids(n_text, gh, gw, r2, d):
+    _check("bf16", 1, 2, n_text, gh, gw, d, r2, seed=1)
 
 
 @pytest.mark.parametrize("splits", [1, 2, 7, 64])

@@ -158,6 +158,22 @@ __device__ __forceinline__ ChunkInfo chunk_info(const ChunkMeta& m, int j, const
 // (square), with the chunk's cell on the grid.  The distance is symmetric, so
 // the same code serves a query column against key rows and a key column
 // against query rows.
+// The lane-mask table of partly admitted chunks (built on the host next to
+// the tile map): for a chunk tile at offset (dy, dx) = (4 iy, 8 ix) from the
+// wavefront's sub-tile, word i has bit l set iff register i of lane l is
+// admitted.  Read through the scalar cache; each word is a lane mask.
+typedef __attribute__((address_space(4))) const uint64_t const_u64_t;
+
+struct MaskTable {
+  const_u64_t* tbl;  // null: no table (masks computed per element)
+  int ky, kx;        // |iy| <= ky, |ix| <= kx
+};
+
+__device__ __forceinline__ void mask_from_table(f32x16_t& s, const MaskTable& mt, int dy, int dx) {
+  const_u64_t* w = mt.tbl + ((((dy >> 2) + mt.ky) * (2 * mt.kx + 1) + (dx >> 3) + mt.kx) << 4);
+  for (int i = 0; i < 16; ++i) s[i] = __builtin_amdgcn_inverse_ballot_w64(w[i]) ? s[i] : -__builtin_inff();
+}
+
 __device__ __forceinline__ void mask_chunk(f32x16_t& s, const ChunkInfo& c, const KeySource& ks, int g,
                                            int cy, int cx, int r2) {
   if (c.tail < 32) {

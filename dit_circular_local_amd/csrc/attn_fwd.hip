@@ -56,6 +56,8 @@ struct Params {
   const uint32_t* tm_offsets;
   const uint32_t* tm_key_tiles;
   const uint16_t* tm_flags;
+  const uint64_t* mask_tbl;  // lane masks of partly admitted chunks (null: computed)
+  int mt_ky, mt_kx;
   int N, n_text, gh, gw, r2, window;
   int ntiles, ntx, nkx;
   uint64_t nkx_magic;
@@ -339,8 +341,12 @@ struct SoftmaxState {
 template <class E>
 __device__ __forceinline__ float chunk_probs(SoftmaxState& sm, f32x16_t& s, const ChunkInfo& c,
                                              const KeySource& ks, int lane, int qy, int qx, int r2,
-                                             float scale_log2, typename E::Probs& pr) {
-  mask_chunk(s, c, ks, lane >> 5, qy, qx, r2);
+                                             float scale_log2, typename E::Probs& pr, const MaskTable& mt,
+                                             int sy0, int sx0) {
+  // a partly admitted key tile wholly on the grid takes its lane masks from
+  // the table; tail chunks and tiles reaching past the grid compute theirs
+  if (c.coord && c.inside && mt.tbl != nullptr) mask_from_table(s, mt, c.ky0 - sy0, c.kx0 - sx0);
+  else mask_chunk(s, c, ks, lane >> 5, qy, qx, r2);
   float mx = s[0];
   for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
   mx = max_xor32(mx);
@@ -371,6 +377,7 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
   if (text_wg && bid >= p.n_text_wg) return;  // padding workgroup (keeps image ids XCD-aligned)
 
   int bh, qtok, qy = 0, qx = 0;
+  int sy0 = 0, sx0 = 0;  // origin of the wavefront's sub-tile (image workgroups)
   bool qvalid;
   KeySource ks;
   ks.n_text = p.n_text;
@@ -421,8 +428,10 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
     const int local = logical - bh * p.band_tiles;
     const int ty = p.band_ty0 + local / p.ntx, tx = local - (local / p.ntx) * p.ntx;
     const int tile = ty * p.ntx + tx;
-    qy = ty * kTileH + wave * kSubH + (qi >> 3);
-    qx = tx * kTileW + (qi & 7);
+    sy0 = ty * kTileH + wave * kSubH;
+    sx0 = tx * kTileW;
+    qy = sy0 + (qi >> 3);
+    qx = sx0 + (qi & 7);
     qvalid = qy >= p.row_begin && qy < p.row_end && qx < p.gw;
     qtok = p.n_text + qy * p.gw + qx;
     ks.dense_base = 0;
@@ -439,6 +448,7 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
   const char* vbase = p.v + head_off;
 
   const DmaPlan<E> plan = make_plan<E>(wave, lane, p.gw);
+  const MaskTable mt{(const_u64_t*)p.mask_tbl, p.mt_ky, p.mt_kx};
 
   E eng;
   eng.load_q(p.q + head_off + (size_t)(qvalid ? qtok : 0) * E::kRowBytes, qvalid, g);
@@ -471,7 +481,7 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
       if (c.active) {
         f32x16_t sc;
         eng.qk(st_cur, lane, sc);
-        alpha = chunk_probs<E>(sm, sc, c, ks, lane, qy, qx, p.r2, p.scale_log2, pr);
+        alpha = chunk_probs<E>(sm, sc, c, ks, lane, qy, qx, p.r2, p.scale_log2, pr, mt, sy0, sx0);
       } else {
         pr.zero();
       }
@@ -610,6 +620,9 @@ int attn_launch(const AttnLaunch& a, void* stream) {
   p.tm_offsets = a.tm_offsets;
   p.tm_key_tiles = a.tm_key_tiles;
   p.tm_flags = a.tm_flags;
+  p.mask_tbl = a.mask_tbl;
+  p.mt_ky = a.mt_ky;
+  p.mt_kx = a.mt_kx;
   p.N = a.n_text + a.gh * a.gw;
   p.n_text = a.n_text;
   p.gh = a.gh;

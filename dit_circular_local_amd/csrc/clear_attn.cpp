@@ -9,6 +9,7 @@
 #include <map>
 #include <mutex>
 #include <tuple>
+#include <vector>
 
 #include "clear_internal.h"
 
@@ -24,6 +25,11 @@ struct TileMapDev {
   uint16_t* flags = nullptr;
   size_t n_entries = 0;
   hipEvent_t ready = nullptr;  // recorded after the build kernels
+  // lane-mask table of partly admitted chunks (null when not built); the host
+  // copy lives as long as the entry, so the upload may run asynchronously
+  uint64_t* mask_tbl = nullptr;
+  int mt_ky = 0, mt_kx = 0;
+  std::vector<uint64_t>* mask_host = nullptr;
 };
 
 struct DevState {
@@ -69,6 +75,20 @@ int get_tile_map(DevState& ds, int gh, int gw, int r2, int window, hipStream_t s
   if (rc) {
     (void)hipFree(m.block);
     return rc;
+  }
+  if (mask_table_dims(g, m.mt_ky, m.mt_kx)) {
+    const size_t words = (size_t)(2 * m.mt_ky + 1) * (2 * m.mt_kx + 1) * 16;
+    m.mask_host = new std::vector<uint64_t>(words);
+    mask_table_fill(g, m.mt_ky, m.mt_kx, m.mask_host->data());
+    if ((e = hipMalloc(&m.mask_tbl, words * 8)) != hipSuccess ||
+        (e = hipMemcpyAsync(m.mask_tbl, m.mask_host->data(), words * 8, hipMemcpyHostToDevice, stream)) !=
+            hipSuccess) {
+      (void)hipStreamSynchronize(stream);
+      if (m.mask_tbl) (void)hipFree(m.mask_tbl);
+      delete m.mask_host;
+      (void)hipFree(m.block);
+      return hip_fail(e, "mask table");
+    }
   }
   if ((e = hipEventCreateWithFlags(&m.ready, hipEventDisableTiming)) != hipSuccess ||
       (e = hipEventRecord(m.ready, stream)) != hipSuccess) {
@@ -229,6 +249,7 @@ int run_forward(const void* q, const void* k, const void* v, void* out, int B, i
   memset(&a, 0, sizeof a);
   a.q = q; a.k = k; a.v = v; a.out = out; a.lse = o.lse_out;
   a.tm_offsets = tm->offsets; a.tm_key_tiles = tm->key_tiles; a.tm_flags = tm->flags;
+  a.mask_tbl = tm->mask_tbl; a.mt_ky = tm->mt_ky; a.mt_kx = tm->mt_kx;
   a.B = B; a.H = H; a.d = d; a.n_text = n_text; a.gh = grid_h; a.gw = grid_w; a.r2 = g.r2;
   a.dtype = o.dtype; a.text_splits = splits; a.window = o.window;
   a.row_begin = strip ? strip->row_begin : 0;
@@ -454,6 +475,8 @@ extern "C" void clear_release_cache(void) {
     for (auto& m : kv.second.maps) {
       if (m.second.ready) (void)hipEventDestroy(m.second.ready);
       (void)hipFree(m.second.block);
+      if (m.second.mask_tbl) (void)hipFree(m.second.mask_tbl);
+      delete m.second.mask_host;
     }
     kv.second.maps.clear();
     if (kv.second.ws) (void)hipFree(kv.second.ws);

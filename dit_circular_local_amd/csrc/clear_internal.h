@@ -19,6 +19,13 @@ size_t tile_map_count(const TileGeom& g);
 void tile_map_fill_host(const TileGeom& g, uint32_t* offsets, uint32_t* key_tiles,
                         uint16_t* flags);
 
+// Lane-mask table of partly admitted chunks (tilemap_host.cpp): entries for
+// tile offsets D = (4 iy, 8 ix), |iy| <= ky, |ix| <= kx, 16 words each.  Not
+// built (false) for r2 < 0 or radii above kMaskTableMaxRadius.
+constexpr int kMaskTableMaxRadius = 256;
+bool mask_table_dims(const TileGeom& g, int& ky, int& kx);
+void mask_table_fill(const TileGeom& g, int ky, int kx, uint64_t* out);
+
 // Device builder: enqueue the kernels that fill offsets / key_tiles / flags
 // (capacity already checked against tile_map_count).
 int tile_map_build_device_launch(const TileGeom& g, uint32_t* offsets, uint32_t* key_tiles,
@@ -36,6 +43,8 @@ struct AttnLaunch {
   const uint32_t* tm_offsets;  // tile map
   const uint32_t* tm_key_tiles;
   const uint16_t* tm_flags;
+  const uint64_t* mask_tbl;   // lane-mask table (NULL: masks computed per element)
+  int mt_ky, mt_kx;
   int B, H, d, n_text, gh, gw, r2;
   int dtype;
   int text_splits;

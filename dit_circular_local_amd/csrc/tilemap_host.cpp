@@ -78,6 +78,43 @@ static int window_validate(int window) {
   return CLEAR_OK;
 }
 
+// Lane masks of partly admitted chunks, for the attention kernels' layout: a
+// wavefront's 32 own cells are a 4 x 8 sub-tile (lane l: row (l % 32) / 8,
+// column l % 8), and accumulator register i of lane group g = l / 32 holds
+// the chunk tile's cell (i / 4, 4 g + i % 4).  Whether a pair is admitted
+// depends only on the offset D = (chunk tile origin - sub-tile origin), a
+// multiple of (4, 8); word i of the entry for D has bit l set iff lane l's
+// register i is admitted.  The window is symmetric, so the same words serve a
+// query sub-tile against key tiles and a key sub-tile against query tiles.
+bool clear::mask_table_dims(const TileGeom& g, int& ky, int& kx) {
+  static_assert(CLEAR_SUB_H == 4 && CLEAR_SUB_W == 8 && CLEAR_KEY_H == 4 && CLEAR_KEY_W == 8,
+                "table layout follows the kernels' tiles");
+  if (g.wmax < 0 || g.wmax > kMaskTableMaxRadius) return false;
+  ky = (g.wmax + CLEAR_KEY_H - 1) / CLEAR_SUB_H;   // |D_y| <= wmax + 3
+  kx = (g.wmax + CLEAR_KEY_W - 1) / CLEAR_SUB_W;   // |D_x| <= wmax + 7
+  return true;
+}
+
+void clear::mask_table_fill(const TileGeom& g, int ky, int kx, uint64_t* out) {
+  const int nx = 2 * kx + 1;
+  for (int iy = -ky; iy <= ky; ++iy)
+    for (int ix = -kx; ix <= kx; ++ix) {
+      uint64_t* e = out + ((size_t)(iy + ky) * nx + (ix + kx)) * 16;
+      for (int i = 0; i < 16; ++i) {
+        uint64_t m = 0;
+        for (int l = 0; l < 64; ++l) {
+          const int qi = l & 31, grp = l >> 5;
+          const long long dy = (qi >> 3) - (i >> 2) - CLEAR_SUB_H * iy;
+          const long long dx = (qi & 7) - (4 * grp + (i & 3)) - CLEAR_SUB_W * ix;
+          const bool in = g.window == kWindowSquare ? (dy * dy <= g.r2 && dx * dx <= g.r2)
+                                                    : dy * dy + dx * dx <= g.r2;
+          if (in) m |= 1ull << l;
+        }
+        e[i] = m;
+      }
+    }
+}
+
 extern "C" int clear_tile_map_size_ex(int window, int grid_h, int grid_w, int r2_max, int tile_h,
                                       int tile_w, int sub_h, int sub_w, int key_h, int key_w,
                                       size_t* n_entries) {

@@ -61,6 +61,8 @@ struct BwdParams {
   const uint32_t* tm_offsets;
   const uint32_t* tm_key_tiles;
   const uint16_t* tm_flags;
+  const uint64_t* mask_tbl;  // lane masks of partly admitted chunks (null: computed)
+  int mt_ky, mt_kx;
   int N, n_text, gh, gw, r2, window;
   int ntiles, ntx, nkx;
   uint64_t nkx_magic;
@@ -349,6 +351,7 @@ __device__ __forceinline__ void stage_bwd(char* st, const ChunkMeta& m, bool den
 // map lists for their tile.  Returns the number of chunks.
 struct WgSetup {
   int bh, tok, cy, cx, split, trow;
+  int sy0, sx0;  // origin of the wavefront's own sub-tile (image workgroups)
   int first;  // the wavefront's first own token (uniform)
   bool valid, text;
 };
@@ -369,6 +372,7 @@ __device__ __forceinline__ int setup_walk(const BwdParams& p, int bid, int wave,
   ks.dense2_base = ks.dense2_limit = 0;
   w.text = bid < p.n_text_wg_pad;
   w.cy = w.cx = 0;
+  w.sy0 = w.sx0 = 0;
   w.split = 0;
   w.trow = 0;
   if (w.text) {
@@ -397,8 +401,10 @@ __device__ __forceinline__ int setup_walk(const BwdParams& p, int bid, int wave,
   w.bh = logical / p.ntiles;
   const int tile = logical - w.bh * p.ntiles;
   const int ty = tile / p.ntx, tx = tile - ty * p.ntx;
-  w.cy = ty * kTileH + wave * kSubH + (li >> 3);
-  w.cx = tx * kTileW + (li & 7);
+  w.sy0 = ty * kTileH + wave * kSubH;
+  w.sx0 = tx * kTileW;
+  w.cy = w.sy0 + (li >> 3);
+  w.cx = w.sx0 + (li & 7);
   w.valid = w.cy < p.gh && w.cx < p.gw;
   w.tok = p.n_text + w.cy * p.gw + w.cx;
   w.first = p.n_text + (ty * kTileH + wave * kSubH) * p.gw + tx * kTileW;
@@ -468,6 +474,7 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_bwd_dkd
   for (int nb = 0; nb < E::kNB; ++nb) dk[nb] = dv[nb] = f32x16_t{};
 
   const BwdPlan<E> plan = make_bwd_plan<E>(wave, lane, p.gw);
+  const MaskTable mt{(const_u64_t*)p.mask_tbl, p.mt_ky, p.mt_kx};
   char* st_cur = smem;
   char* st_nxt = smem + L::kStageABS;
   if (n > 0) {
@@ -483,7 +490,8 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_bwd_dkd
         E::row_mma(st_cur + L::kA, lane, kr, s);
         if constexpr (E::kOwnInLds) E::row_mma_own(st_cur + L::kB, own_v, lane, dp);
         else E::row_mma(st_cur + L::kB, lane, vr, dp);
-        mask_chunk(s, c, ks, g, w.cy, w.cx, p.r2);
+        if (c.coord && c.inside && mt.tbl != nullptr) mask_from_table(s, mt, c.ky0 - w.sy0, c.kx0 - w.sx0);
+        else mask_chunk(s, c, ks, g, w.cy, w.cx, p.r2);
         const float* sv = (const float*)(st_cur + L::kStats + 256 * wave);
         for (int a = 0; a < 4; ++a) {
           const f32x4_t l2 = *(const f32x4_t*)(sv + 8 * a + 4 * g);
@@ -550,6 +558,7 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_bwd_dq_
   for (int nb = 0; nb < E::kNB; ++nb) dq[nb] = f32x16_t{};
 
   const BwdPlan<E> plan = make_bwd_plan<E>(wave, lane, p.gw);
+  const MaskTable mt{(const_u64_t*)p.mask_tbl, p.mt_ky, p.mt_kx};
   char* st_cur = smem;
   char* st_nxt = smem + L::kStageAB;
   if (n > 0) {
@@ -564,7 +573,8 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_bwd_dq_
         f32x16_t s, dp;
         E::row_mma(st_cur + L::kA, lane, qr, s);
         E::row_mma(st_cur + L::kB, lane, dor, dp);
-        mask_chunk(s, c, ks, g, w.cy, w.cx, p.r2);
+        if (c.coord && c.inside && mt.tbl != nullptr) mask_from_table(s, mt, c.ky0 - w.sy0, c.kx0 - w.sx0);
+        else mask_chunk(s, c, ks, g, w.cy, w.cx, p.r2);
         for (int i = 0; i < 16; ++i) {
           const float pr = __builtin_amdgcn_exp2f(fmaf(s[i], p.scale_log2, -stq.x));
           dp[i] = pr * (dp[i] - stq.y);
@@ -694,6 +704,9 @@ int attn_bwd_launch(const BwdLaunch& a, void* stream) {
   p.tm_offsets = a.tm_offsets;
   p.tm_key_tiles = a.tm_key_tiles;
   p.tm_flags = a.tm_flags;
+  p.mask_tbl = a.mask_tbl;
+  p.mt_ky = a.mt_ky;
+  p.mt_kx = a.mt_kx;
   p.N = a.n_text + a.gh * a.gw;
   p.n_text = a.n_text;
   p.gh = a.gh;

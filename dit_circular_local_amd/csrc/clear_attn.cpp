@@ -352,6 +352,7 @@ int run_backward(const void* q, const void* k, const void* v, const void* out, c
     a.ws_dv = (float*)((char*)ws + stats_bytes + 2 * part_bytes);
   }
   a.tm_offsets = tm->offsets; a.tm_key_tiles = tm->key_tiles; a.tm_flags = tm->flags;
+  a.mask_tbl = tm->mask_tbl; a.mt_ky = tm->mt_ky; a.mt_kx = tm->mt_kx;
   a.B = B; a.H = H; a.d = d; a.n_text = n_text; a.gh = grid_h; a.gw = grid_w; a.r2 = g.r2;
   a.dtype = o.dtype; a.text_splits = splits; a.window = o.window;
   rc = attn_bwd_launch(a, stream);

@@ -74,6 +74,8 @@ struct BwdLaunch {
   const uint32_t* tm_offsets;
   const uint32_t* tm_key_tiles;
   const uint16_t* tm_flags;
+  const uint64_t* mask_tbl;   // lane-mask table (NULL: masks computed per element)
+  int mt_ky, mt_kx;
   int B, H, d, n_text, gh, gw, r2;
   int dtype;
   int text_splits;

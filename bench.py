@@ -91,11 +91,21 @@ FWD_KERNEL_SOURCES = ("dit_circular_local_amd/csrc/attn_fwd.hip", "dit_circular_
                       "include/clear_attn.h")
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace collapsed: edits to
+    comments leave the hash (and the compiled kernel) unchanged."""
+    import re
+
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for name in FWD_KERNEL_SOURCES:
-        with open(os.path.join(ROOT, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(ROOT, name), encoding="utf-8") as f:
+            h.update(name.encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

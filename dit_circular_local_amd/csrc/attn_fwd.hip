@@ -12,7 +12,8 @@
 //    chunks of 32: first the text keys, then the 4 x 8 cell key tiles the tile
 //    map lists for the query tile.  A wavefront skips key tiles its sub-tile does
 //    not touch and applies the per-element circular mask only to key tiles it
-//    does not fully admit;
+//    does not fully admit (one select per element, its lane mask read from a
+//    small table indexed by the tile's offset from the sub-tile);
 //  * text workgroups: 128 text queries against a contiguous range of all keys
 //    (the range is one of `splits` parts; partial results are merged exactly by
 //    log-sum-exp in a second kernel when splits > 1).

@@ -51,7 +51,7 @@ __device__ __forceinline__ int acc_row(int i, int g) { return 8 * (i >> 2) + 4 *
 // Wave-wide combine of a value with its partner lane l ^ 32.
 __device__ __forceinline__ float max_xor32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_xor32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -96,25 +96,29 @@ struct ChunkMeta {
   int ky0, kx0;   // key-tile origin (image chunks)
 };
 
-__device__ __forceinline__ ChunkMeta chunk_meta(const KeySource& ks, int j) {
+// Chunk j >= n_dense: entry j - n_dense of the query tile's key-tile list.
+__device__ __forceinline__ ChunkMeta tile_chunk_meta(const KeySource& ks, int j) {
   ChunkMeta m;
-  if (j < ks.n_dense) {
-    const bool first = j < ks.n_dense1;
-    m.tok0 = first ? ks.dense_base + j * kChunk : ks.dense2_base + (j - ks.n_dense1) * kChunk;
-    m.limit = first ? ks.dense_limit : ks.dense2_limit;
-    m.flag = 0;
-    m.ky0 = 0;
-    m.kx0 = 0;
-  } else {
-    const int e = ks.e0 + j - ks.n_dense;
-    const uint32_t kt = ks.key_tiles[e];
-    m.flag = (ks.flags32[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-    const int kty = (int)(((uint64_t)kt * ks.nkx_magic) >> 32);
-    m.ky0 = kty * kKeyH;
-    m.kx0 = ((int)kt - kty * ks.nkx) * kKeyW;
-    m.tok0 = ks.n_text + m.ky0 * ks.gw + m.kx0;
-    m.limit = 0;
-  }
+  const int e = ks.e0 + j - ks.n_dense;
+  const uint32_t kt = ks.key_tiles[e];
+  m.flag = (ks.flags32[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+  const int kty = (int)(((uint64_t)kt * ks.nkx_magic) >> 32);
+  m.ky0 = kty * kKeyH;
+  m.kx0 = ((int)kt - kty * ks.nkx) * kKeyW;
+  m.tok0 = ks.n_text + m.ky0 * ks.gw + m.kx0;
+  m.limit = 0;
+  return m;
+}
+
+__device__ __forceinline__ ChunkMeta chunk_meta(const KeySource& ks, int j) {
+  if (j >= ks.n_dense) return tile_chunk_meta(ks, j);
+  ChunkMeta m;
+  const bool first = j < ks.n_dense1;
+  m.tok0 = first ? ks.dense_base + j * kChunk : ks.dense2_base + (j - ks.n_dense1) * kChunk;
+  m.limit = first ? ks.dense_limit : ks.dense2_limit;
+  m.flag = 0;
+  m.ky0 = 0;
+  m.kx0 = 0;
   return m;
 }
 
@@ -134,18 +138,22 @@ struct ChunkInfo {
   int ky0, kx0;
 };
 
+// A dense chunk: every wavefront computes it; positions past the range's
+// limit are masked.
+__device__ __forceinline__ ChunkInfo dense_chunk_info(const ChunkMeta& m, const KeySource& ks) {
+  const int rem = m.limit - m.tok0;
+  return ChunkInfo{true, false, ks.window == 1, true, rem < kChunk ? rem : kChunk, m.ky0, m.kx0};
+}
+
+// A key tile: computed by the wavefronts whose sub-tile touches it, masked
+// by coordinates unless the sub-tile admits all of it.
+__device__ __forceinline__ ChunkInfo tile_chunk_info(const ChunkMeta& m, const KeySource& ks, int wave) {
+  return ChunkInfo{((m.flag >> wave) & 1u) != 0, ((m.flag >> (8 + wave)) & 1u) == 0, ks.window == 1,
+                   m.ky0 + kKeyH <= ks.gh && m.kx0 + kKeyW <= ks.gw, kChunk, m.ky0, m.kx0};
+}
+
 __device__ __forceinline__ ChunkInfo chunk_info(const ChunkMeta& m, int j, const KeySource& ks, int wave) {
-  ChunkInfo c{true, false, false, true, 32, m.ky0, m.kx0};
-  c.square = ks.window == 1;
-  if (j < ks.n_dense) {
-    const int rem = m.limit - m.tok0;
-    c.tail = rem < 32 ? rem : 32;
-  } else {
-    c.active = (m.flag >> wave) & 1u;
-    c.coord = !((m.flag >> (8 + wave)) & 1u);
-    c.inside = m.ky0 + kKeyH <= ks.gh && m.kx0 + kKeyW <= ks.gw;
-  }
-  return c;
+  return j < ks.n_dense ? dense_chunk_info(m, ks) : tile_chunk_info(m, ks, wave);
 }
 
 

@@ -121,9 +121,9 @@ struct Bf16 {
   __device__ void settle_q() {
     for (int kk = 0; kk < kKK; ++kk) asm volatile("" ::"v"(q[kk]));
   }
-  __device__ void qk(const char* st, int lane, f32x16_t& s) const {
+  __device__ void qk(const char* st, int lane, f32x16_t& s, const f32x16_t& init) const {
     const char* kb = st + kKOff + (lane & 31) * kRowK + (lane >> 5) * 16;
-    s = f32x16_t{};
+    s = init;
     for (int kk = 0; kk < kKK; ++kk) {
       bf16x8_t a = *(const bf16x8_t*)(kb + kk * 32);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q[kk], s, 0, 0, 0);
@@ -137,9 +137,8 @@ struct Bf16 {
     bf16x8_t b[2];
     __device__ void zero() { b[0] = b[1] = bf16x8_t{}; }
   };
-  __device__ static float probs(const f32x16_t& e, Probs& pr) {
+  __device__ static void probs(const f32x16_t& e, Probs& pr, float& l) {
     const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
-    float l = 0.0f;
     for (int t = 0; t < 2; ++t)
       for (int j = 0; j < 4; ++j) {
         const bf16x2_t h = __builtin_convertvector(f32x2_t{e[8 * t + 2 * j], e[8 * t + 2 * j + 1]}, bf16x2_t);
@@ -147,7 +146,6 @@ struct Bf16 {
         pr.b[t][2 * j + 1] = h[1];
         l = __builtin_amdgcn_fdot2_f32_bf16(h, one, l, false);
       }
-    return l;
   }
   // O^T += V^T P^T.  The A operand (lane l: d = 32*nb + l % 32, eight keys of
   // lane group g = l / 32) comes from two transpose loads: in each 16-lane group,
@@ -224,9 +222,9 @@ struct F32 {
   __device__ void settle_q() {
     for (int i = 0; i < kHalf; ++i) asm volatile("" ::"v"(q[i]));
   }
-  __device__ void qk(const char* st, int lane, f32x16_t& s) const {
+  __device__ void qk(const char* st, int lane, f32x16_t& s, const f32x16_t& init) const {
     const char* kb = st + kKOff + (lane & 31) * kRowK + (lane >> 5) * kHalf * 4;
-    s = f32x16_t{};
+    s = init;
     for (int s4 = 0; s4 < kHalf / 4; ++s4) {
       f32x4_t a = *(const f32x4_t*)(kb + s4 * 16);
       for (int e = 0; e < 4; ++e)
@@ -237,11 +235,9 @@ struct F32 {
     f32x16_t p;
     __device__ void zero() { p = f32x16_t{}; }
   };
-  __device__ static float probs(const f32x16_t& e, Probs& pr) {
-    float l = 0.0f;
+  __device__ static void probs(const f32x16_t& e, Probs& pr, float& l) {
     for (int i = 0; i < 16; ++i) l += e[i];
     pr.p = e;
-    return l;
   }
   __device__ void pv(const char* st, int lane, const Probs& pr) {
     const f32x16_t& p = pr.p;
@@ -333,35 +329,57 @@ __device__ __forceinline__ void stage_chunk(char* st, const ChunkMeta& m, bool d
 
 struct SoftmaxState {
   float M, L;
+  float T;  // raw logit above which the reference max moves: (M + tau) / scale_log2
 };
 
-// Logits of one chunk -> masked, online-softmax probabilities (base 2, lazy
-// reference max).  Returns the factor O must be scaled by before this chunk's
-// P.V (1 unless the reference max moved); O itself is not touched here, so the
-// caller can skip this step for a chunk the wavefront does not touch.
+// Online-softmax step of one chunk's masked logits (base 2, lazy reference
+// max): row max over the lane pair, a rescale only when some row's max passes
+// its threshold, probabilities into pr and their sum into L.  Returns true (the
+// same on every lane) when the reference max moved; alpha is then the factor O
+// must be scaled by before this chunk's P.V.  O itself is not touched here, so
+// the caller can skip this step for a chunk the wavefront does not touch.
 template <class E>
-__device__ __forceinline__ float chunk_probs(SoftmaxState& sm, f32x16_t& s, const ChunkInfo& c,
-                                             const KeySource& ks, int lane, int qy, int qx, int r2,
-                                             float scale_log2, typename E::Probs& pr, const MaskTable& mt,
-                                             int sy0, int sx0) {
-  // a partly admitted key tile wholly on the grid takes its lane masks from
-  // the table; tail chunks and tiles reaching past the grid compute theirs
-  if (c.coord && c.inside && mt.tbl != nullptr) mask_from_table(s, mt, c.ky0 - sy0, c.kx0 - sx0);
-  else mask_chunk(s, c, ks, lane >> 5, qy, qx, r2);
+__device__ __forceinline__ bool chunk_softmax(SoftmaxState& sm, f32x16_t& s, float scale_log2,
+                                              float inv_scale_log2, typename E::Probs& pr, float& alpha) {
   float mx = s[0];
-  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+  for (int i = 1; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, s[i]);
   mx = max_xor32(mx);
-  const float mxs = mx * scale_log2;
-  float alpha = 1.0f;
-  if (__ballot(mxs > sm.M + kLazyTau) != 0ull) {
-    const float Mn = fmaxf(sm.M, mxs);
+  bool moved = false;
+  if (__ballot(mx > sm.T) != 0ull) {
+    const float Mn = fmaxf(sm.M, mx * scale_log2);
     alpha = __builtin_amdgcn_exp2f(sm.M - Mn);
     sm.L *= alpha;
     sm.M = Mn;
+    sm.T = (Mn + kLazyTau) * inv_scale_log2;
+    moved = true;
   }
   for (int i = 0; i < 16; ++i) s[i] = __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -sm.M));
-  sm.L += E::probs(s, pr);
-  return alpha;
+  E::probs(s, pr, sm.L);
+  return moved;
+}
+
+// Logits of one chunk.  A partly admitted chunk starts Q.K from its mask as
+// the accumulator, 0 where the pair is admitted and -inf elsewhere, so the
+// mask costs no pass over the logits and a whole chunk none at all.  A key
+// tile wholly on the grid takes its lane masks from the table; tail chunks and
+// tiles reaching past the grid compute theirs.  Each branch keeps its own
+// products (the empty statements differ, so they are not merged): joined
+// before the products, the branches would meet on the sixteen accumulator
+// registers, and the whole chunk would pay for zeroing them.
+template <class E>
+__device__ __forceinline__ void chunk_logits(const E& eng, const char* st, int lane, f32x16_t& s,
+                                             const ChunkInfo& c, const KeySource& ks, int qy, int qx, int r2,
+                                             const MaskTable& mt, int sy0, int sx0) {
+  if (c.coord || c.tail < kChunk) {
+    f32x16_t bias{};
+    if (c.coord && c.inside && mt.tbl != nullptr) mask_from_table(bias, mt, c.ky0 - sy0, c.kx0 - sx0);
+    else mask_chunk(bias, c, ks, lane >> 5, qy, qx, r2);
+    eng.qk(st, lane, s, bias);
+    asm volatile("; masked chunk" : "+v"(s));
+  } else {
+    eng.qk(st, lane, s, f32x16_t{});
+    asm volatile("; whole chunk" : "+v"(s));
+  }
 }
 
 template <class E>
@@ -454,7 +472,8 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
   E eng;
   eng.load_q(p.q + head_off + (size_t)(qvalid ? qtok : 0) * E::kRowBytes, qvalid, g);
   eng.zero_o();
-  SoftmaxState sm{kMInit, 0.0f};
+  const float inv_scale_log2 = 1.0f / p.scale_log2;
+  SoftmaxState sm{kMInit, 0.0f, (kMInit + kLazyTau) * inv_scale_log2};
 
   // ---- chunk loop.  Two LDS stages: after the barrier of iteration j, chunk
   // j is in stage j % 2 (its direct-to-LDS loads were issued in iteration
@@ -470,29 +489,46 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
     ChunkMeta m_cur = chunk_meta(ks, 0);
     ChunkMeta m_nxt = chunk_meta(ks, n > 1 ? 1 : 0);
     stage_chunk<E>(st_cur, m_cur, 0 < ks.n_dense, wave, ks, kbase, vbase, plan);
-    for (int j = 0; j < n; ++j) {
-      __syncthreads();
-      if (j + 1 < n) stage_chunk<E>(st_nxt, m_nxt, j + 1 < ks.n_dense, wave, ks, kbase, vbase, plan);
-      const ChunkInfo c = chunk_info(m_cur, j, ks, wave);
-      // A chunk the wavefront's sub-tile does not touch skips Q.K and the
-      // softmax: its probabilities are zero.  P.V and the rescale of O stay
-      // outside the branch, so O is updated on one path only.
+    // One chunk.  A chunk the wavefront's sub-tile does not touch skips Q.K
+    // and the softmax: its probabilities are zero.  P.V and the rescale of O
+    // stay outside that branch, so O is updated on one path only.
+    auto compute = [&](const ChunkInfo& c) {
       typename E::Probs pr;
       float alpha = 1.0f;
+      bool moved = false;
       if (c.active) {
         f32x16_t sc;
-        eng.qk(st_cur, lane, sc);
-        alpha = chunk_probs<E>(sm, sc, c, ks, lane, qy, qx, p.r2, p.scale_log2, pr, mt, sy0, sx0);
+        chunk_logits(eng, st_cur, lane, sc, c, ks, qy, qx, p.r2, mt, sy0, sx0);
+        moved = chunk_softmax<E>(sm, sc, p.scale_log2, inv_scale_log2, pr, alpha);
       } else {
         pr.zero();
       }
-      if (__ballot(alpha != 1.0f) != 0ull) eng.scale_o(alpha);
+      if (moved) eng.scale_o(alpha);
       eng.pv(st_cur, lane, pr);
-      m_cur = m_nxt;
-      m_nxt = chunk_meta(ks, j + 2 < n ? j + 2 : n - 1);
       char* t = st_cur;
       st_cur = st_nxt;
       st_nxt = t;
+    };
+    // The dense chunks come first (the text keys of an image workgroup, all
+    // of a text workgroup's chunks); the one after the last may be a key tile.
+    // Each kind of chunk has a loop of its own, which carries only that
+    // kind's state and tests.
+    int j = 0;
+    for (; j < ks.n_dense; ++j) {
+      __syncthreads();
+      if (j + 1 < n) stage_chunk<E>(st_nxt, m_nxt, j + 1 < ks.n_dense, wave, ks, kbase, vbase, plan);
+      const ChunkInfo c = dense_chunk_info(m_cur, ks);
+      m_cur = m_nxt;
+      m_nxt = chunk_meta(ks, j + 2 < n ? j + 2 : n - 1);
+      compute(c);
+    }
+    for (; j < n; ++j) {
+      __syncthreads();
+      if (j + 1 < n) stage_chunk<E>(st_nxt, m_nxt, false, wave, ks, kbase, vbase, plan);
+      const ChunkInfo c = tile_chunk_info(m_cur, ks, wave);
+      m_cur = m_nxt;
+      m_nxt = tile_chunk_meta(ks, j + 2 < n ? j + 2 : n - 1);
+      compute(c);
     }
   }
 

@@ -59,13 +59,11 @@ struct BwdParams {
   float* ws_dk;
   float* ws_dv;
   const uint32_t* tm_offsets;
-  const uint32_t* tm_key_tiles;
-  const uint16_t* tm_flags;
+  const uint32_t* tm_desc;
   const uint64_t* mask_tbl;  // lane masks of partly admitted chunks (null: computed)
   int mt_ky, mt_kx;
   int N, n_text, gh, gw, r2, window;
-  int ntiles, ntx, nkx;
-  uint64_t nkx_magic;
+  int ntiles, ntx;
   int n_text_blocks, splits, chunks_per_split;
   int n_text_wg, n_text_wg_pad, n_img_wg, BH;
   float scale_log2, scale;
@@ -362,10 +360,7 @@ __device__ __forceinline__ int setup_walk(const BwdParams& p, int bid, int wave,
   ks.n_text = p.n_text;
   ks.gh = p.gh;
   ks.gw = p.gw;
-  ks.nkx = p.nkx;
-  ks.nkx_magic = p.nkx_magic;
-  ks.key_tiles = (const_u32_t*)p.tm_key_tiles;
-  ks.flags32 = (const_u32_t*)p.tm_flags;
+  ks.desc = (const_u32x4_t*)p.tm_desc;
   ks.e0 = 0;
   ks.n_tok = p.N;
   ks.window = p.window;
@@ -702,8 +697,7 @@ int attn_bwd_launch(const BwdLaunch& a, void* stream) {
   p.ws_dk = a.ws_dk;
   p.ws_dv = a.ws_dv;
   p.tm_offsets = a.tm_offsets;
-  p.tm_key_tiles = a.tm_key_tiles;
-  p.tm_flags = a.tm_flags;
+  p.tm_desc = a.tm_desc;
   p.mask_tbl = a.mask_tbl;
   p.mt_ky = a.mt_ky;
   p.mt_kx = a.mt_kx;
@@ -715,8 +709,6 @@ int attn_bwd_launch(const BwdLaunch& a, void* stream) {
   p.window = a.window;
   p.ntx = (a.gw + kTileW - 1) / kTileW;
   p.ntiles = ((a.gh + kTileH - 1) / kTileH) * p.ntx;
-  p.nkx = (a.gw + kKeyW - 1) / kKeyW;
-  p.nkx_magic = ((1ull << 32) + (uint64_t)p.nkx - 1) / (uint64_t)p.nkx;
   p.BH = a.B * a.H;
   p.n_text_blocks = (a.n_text + kTextRows - 1) / kTextRows;
   const int nall = (p.N + kChunk - 1) / kChunk;

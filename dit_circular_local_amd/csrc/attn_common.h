@@ -22,6 +22,7 @@ typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+typedef __attribute__((address_space(4))) const u32x4_t const_u32x4_t;
 typedef __attribute__((ext_vector_type(2))) short s16x2_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((ext_vector_type(8))) short s16x8_t;
@@ -72,13 +73,11 @@ struct KeySource {
   // dense chunks 0 .. n_dense1-1 cover tokens [dense_base, dense_limit), chunks
   // n_dense1 .. n_dense-1 cover [dense2_base, dense2_limit)
   int dense_base, dense_limit, n_dense1, dense2_base, dense2_limit, n_dense;
-  int n_text, gh, gw, nkx;
-  uint64_t nkx_magic;    // ceil(2^32 / nkx): kt / nkx == (kt * magic) >> 32 here
+  int n_text, gh, gw;
   int e0;                // the query tile's first tile-map entry
   int window;            // 0 circle, 1 square
   int n_tok;             // tokens per head (N)
-  const_u32_t* key_tiles;  // whole tile map, read through the scalar cache
-  const_u32_t* flags32;    // u16 flags, two per word
+  const_u32x4_t* desc;   // tile-map entry descriptors, read through the scalar cache
 };
 
 // Buffer resource over `bytes` bytes from a uniform address (gfx9 resource
@@ -91,35 +90,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_rsrc(const char* base, ui
 // mask needs.
 struct ChunkMeta {
   int tok0;       // first key token of the chunk
+  int left;       // tokens from tok0 to the end of the head
   int limit;      // dense chunks: end of the chunk's token range
-  unsigned flag;  // tile-map flags (0 for dense chunks)
-  int ky0, kx0;   // key-tile origin (image chunks)
+  unsigned flag;  // tile-map flags and kTileInside (0 for dense chunks)
+  unsigned kt;    // key tiles: (row << 16) | column of the tile
 };
 
-// Chunk j >= n_dense: entry j - n_dense of the query tile's key-tile list.
+// Chunk j >= n_dense: entry j - n_dense of the query tile's key-tile list,
+// from its descriptor (one scalar load).
 __device__ __forceinline__ ChunkMeta tile_chunk_meta(const KeySource& ks, int j) {
-  ChunkMeta m;
-  const int e = ks.e0 + j - ks.n_dense;
-  const uint32_t kt = ks.key_tiles[e];
-  m.flag = (ks.flags32[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-  const int kty = (int)(((uint64_t)kt * ks.nkx_magic) >> 32);
-  m.ky0 = kty * kKeyH;
-  m.kx0 = ((int)kt - kty * ks.nkx) * kKeyW;
-  m.tok0 = ks.n_text + m.ky0 * ks.gw + m.kx0;
-  m.limit = 0;
-  return m;
+  const u32x4_t d = ks.desc[ks.e0 + j - ks.n_dense];
+  return ChunkMeta{ks.n_text + (int)d[0], (int)d[3], 0, d[1], d[2]};
 }
 
 __device__ __forceinline__ ChunkMeta chunk_meta(const KeySource& ks, int j) {
   if (j >= ks.n_dense) return tile_chunk_meta(ks, j);
-  ChunkMeta m;
   const bool first = j < ks.n_dense1;
-  m.tok0 = first ? ks.dense_base + j * kChunk : ks.dense2_base + (j - ks.n_dense1) * kChunk;
-  m.limit = first ? ks.dense_limit : ks.dense2_limit;
-  m.flag = 0;
-  m.ky0 = 0;
-  m.kx0 = 0;
-  return m;
+  const int tok0 = first ? ks.dense_base + j * kChunk : ks.dense2_base + (j - ks.n_dense1) * kChunk;
+  return ChunkMeta{tok0, ks.n_tok - tok0, first ? ks.dense_limit : ks.dense2_limit, 0u, 0u};
 }
 
 // Offset of a padding slot: past any buffer bound, so its load returns zeros.
@@ -135,21 +123,23 @@ struct ChunkInfo {
   bool square;  // square-window variant
   bool inside;  // key tile wholly on the grid
   int tail;     // dense chunk: positions >= tail are masked
-  int ky0, kx0;
+  int kty, ktx; // key tile's row and column (key-tile chunks)
+  int ky0, kx0; // its first cell
 };
 
 // A dense chunk: every wavefront computes it; positions past the range's
 // limit are masked.
 __device__ __forceinline__ ChunkInfo dense_chunk_info(const ChunkMeta& m, const KeySource& ks) {
   const int rem = m.limit - m.tok0;
-  return ChunkInfo{true, false, ks.window == 1, true, rem < kChunk ? rem : kChunk, m.ky0, m.kx0};
+  return ChunkInfo{true, false, ks.window == 1, true, rem < kChunk ? rem : kChunk, 0, 0, 0, 0};
 }
 
 // A key tile: computed by the wavefronts whose sub-tile touches it, masked
 // by coordinates unless the sub-tile admits all of it.
 __device__ __forceinline__ ChunkInfo tile_chunk_info(const ChunkMeta& m, const KeySource& ks, int wave) {
+  const int kty = (int)(m.kt >> 16), ktx = (int)(m.kt & 0xffffu);
   return ChunkInfo{((m.flag >> wave) & 1u) != 0, ((m.flag >> (8 + wave)) & 1u) == 0, ks.window == 1,
-                   m.ky0 + kKeyH <= ks.gh && m.kx0 + kKeyW <= ks.gw, kChunk, m.ky0, m.kx0};
+                   (m.flag & kTileInside) != 0, kChunk, kty, ktx, kty * kKeyH, ktx * kKeyW};
 }
 
 __device__ __forceinline__ ChunkInfo chunk_info(const ChunkMeta& m, int j, const KeySource& ks, int wave) {
@@ -177,9 +167,20 @@ struct MaskTable {
   int ky, kx;        // |iy| <= ky, |ix| <= kx
 };
 
-__device__ __forceinline__ void mask_from_table(f32x16_t& s, const MaskTable& mt, int dy, int dx) {
-  const_u64_t* w = mt.tbl + ((((dy >> 2) + mt.ky) * (2 * mt.kx + 1) + (dx >> 3) + mt.kx) << 4);
+// Apply the sixteen lane masks at w (word i masks register i).
+__device__ __forceinline__ void apply_lane_masks(f32x16_t& s, const_u64_t* w) {
   for (int i = 0; i < 16; ++i) s[i] = __builtin_amdgcn_inverse_ballot_w64(w[i]) ? s[i] : -__builtin_inff();
+}
+
+__device__ __forceinline__ void mask_from_table(f32x16_t& s, const MaskTable& mt, int dy, int dx) {
+  apply_lane_masks(s, mt.tbl + ((((dy >> 2) + mt.ky) * (2 * mt.kx + 1) + (dx >> 3) + mt.kx) << 4));
+}
+
+// Table row of a wavefront whose sub-tile starts at cell (sy0, sx0), a
+// multiple of (4, 8): the words of key tile (kty, ktx) start at entry
+// kty * (2 kx + 1) + ktx + table_base(mt, sy0, sx0).
+__device__ __forceinline__ int table_base(const MaskTable& mt, int sy0, int sx0) {
+  return (mt.ky - (sy0 >> 2)) * (2 * mt.kx + 1) + mt.kx - (sx0 >> 3);
 }
 
 __device__ __forceinline__ void mask_chunk(f32x16_t& s, const ChunkInfo& c, const KeySource& ks, int g,

@@ -55,13 +55,11 @@ struct Params {
   float* ws_o;
   float* ws_ml;
   const uint32_t* tm_offsets;
-  const uint32_t* tm_key_tiles;
-  const uint16_t* tm_flags;
+  const uint32_t* tm_desc;
   const uint64_t* mask_tbl;  // lane masks of partly admitted chunks (null: computed)
   int mt_ky, mt_kx;
   int N, n_text, gh, gw, r2, window;
-  int ntiles, ntx, nkx;
-  uint64_t nkx_magic;
+  int ntiles, ntx;
   int n_text_blocks, splits, chunks_per_split;
   int n_text_wg, n_text_wg_pad, n_img_wg, BH;
   // image rows computed: [row_begin, row_end), i.e. query-tile rows
@@ -315,8 +313,8 @@ __device__ __forceinline__ void stage_chunk(char* st, const ChunkMeta& m, bool d
                                             const KeySource& ks, const char* kbase, const char* vbase,
                                             const DmaPlan<E>& pl) {
   const size_t base = (size_t)m.tok0 * E::kRowBytes;
-  const size_t left = (size_t)(ks.n_tok - m.tok0) * E::kRowBytes;
-  const uint32_t bytes = left < 0x7fffffffu ? (uint32_t)left : 0x7fffffffu;
+  constexpr int kMaxLeft = 0x7fffffff / E::kRowBytes;  // a resource covers < 2 GB
+  const uint32_t bytes = (uint32_t)(m.left < kMaxLeft ? m.left : kMaxLeft) * E::kRowBytes;
   const __amdgpu_buffer_rsrc_t rk = byte_rsrc(kbase + base, bytes), rv = byte_rsrc(vbase + base, bytes);
   if (dense) {
     dma_blocks<E>(st, wave, rk, rv, pl.dense_k, pl.dense_v);
@@ -369,10 +367,11 @@ __device__ __forceinline__ bool chunk_softmax(SoftmaxState& sm, f32x16_t& s, flo
 template <class E>
 __device__ __forceinline__ void chunk_logits(const E& eng, const char* st, int lane, f32x16_t& s,
                                              const ChunkInfo& c, const KeySource& ks, int qy, int qx, int r2,
-                                             const MaskTable& mt, int sy0, int sx0) {
+                                             const MaskTable& mt, int mt_base) {
   if (c.coord || c.tail < kChunk) {
     f32x16_t bias{};
-    if (c.coord && c.inside && mt.tbl != nullptr) mask_from_table(bias, mt, c.ky0 - sy0, c.kx0 - sx0);
+    if (c.coord && c.inside && mt.tbl != nullptr)
+      apply_lane_masks(bias, mt.tbl + ((c.kty * (2 * mt.kx + 1) + c.ktx + mt_base) << 4));
     else mask_chunk(bias, c, ks, lane >> 5, qy, qx, r2);
     eng.qk(st, lane, s, bias);
     asm volatile("; masked chunk" : "+v"(s));
@@ -402,10 +401,7 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
   ks.n_text = p.n_text;
   ks.gh = p.gh;
   ks.gw = p.gw;
-  ks.nkx = p.nkx;
-  ks.nkx_magic = p.nkx_magic;
-  ks.key_tiles = (const_u32_t*)p.tm_key_tiles;
-  ks.flags32 = (const_u32_t*)p.tm_flags;
+  ks.desc = (const_u32x4_t*)p.tm_desc;
   ks.e0 = 0;
   ks.n_tok = p.N;
   ks.window = p.window;
@@ -468,6 +464,7 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
 
   const DmaPlan<E> plan = make_plan<E>(wave, lane, p.gw);
   const MaskTable mt{(const_u64_t*)p.mask_tbl, p.mt_ky, p.mt_kx};
+  const int mt_base = table_base(mt, sy0, sx0);
 
   E eng;
   eng.load_q(p.q + head_off + (size_t)(qvalid ? qtok : 0) * E::kRowBytes, qvalid, g);
@@ -492,22 +489,19 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
     // One chunk.  A chunk the wavefront's sub-tile does not touch skips Q.K
     // and the softmax: its probabilities are zero.  P.V and the rescale of O
     // stay outside that branch, so O is updated on one path only.
-    auto compute = [&](const ChunkInfo& c) {
+    auto compute = [&](const ChunkInfo& c, const char* st) {
       typename E::Probs pr;
       float alpha = 1.0f;
       bool moved = false;
       if (c.active) {
         f32x16_t sc;
-        chunk_logits(eng, st_cur, lane, sc, c, ks, qy, qx, p.r2, mt, sy0, sx0);
+        chunk_logits(eng, st, lane, sc, c, ks, qy, qx, p.r2, mt, mt_base);
         moved = chunk_softmax<E>(sm, sc, p.scale_log2, inv_scale_log2, pr, alpha);
       } else {
         pr.zero();
       }
       if (moved) eng.scale_o(alpha);
-      eng.pv(st_cur, lane, pr);
-      char* t = st_cur;
-      st_cur = st_nxt;
-      st_nxt = t;
+      eng.pv(st, lane, pr);
     };
     // The dense chunks come first (the text keys of an image workgroup, all
     // of a text workgroup's chunks); the one after the last may be a key tile.
@@ -520,16 +514,27 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
       const ChunkInfo c = dense_chunk_info(m_cur, ks);
       m_cur = m_nxt;
       m_nxt = chunk_meta(ks, j + 2 < n ? j + 2 : n - 1);
-      compute(c);
+      compute(c, st_cur);
+      char* t = st_cur;
+      st_cur = st_nxt;
+      st_nxt = t;
     }
-    for (; j < n; ++j) {
+    // Key tiles, two per trip so that the stages and the two descriptors in
+    // flight keep fixed roles (no copies between iterations): mc describes
+    // chunk jj (staged in cur), mn chunk jj + 1 (to be staged in nxt), and mc
+    // then receives chunk jj + 2.
+    auto tile_step = [&](int jj, ChunkMeta& mc, const ChunkMeta& mn, const char* cur, char* nxt) {
       __syncthreads();
-      if (j + 1 < n) stage_chunk<E>(st_nxt, m_nxt, false, wave, ks, kbase, vbase, plan);
-      const ChunkInfo c = tile_chunk_info(m_cur, ks, wave);
-      m_cur = m_nxt;
-      m_nxt = tile_chunk_meta(ks, j + 2 < n ? j + 2 : n - 1);
-      compute(c);
+      if (jj + 1 < n) stage_chunk<E>(nxt, mn, false, wave, ks, kbase, vbase, plan);
+      const ChunkInfo c = tile_chunk_info(mc, ks, wave);
+      mc = tile_chunk_meta(ks, jj + 2 < n ? jj + 2 : n - 1);
+      compute(c, cur);
+    };
+    for (; j + 1 < n; j += 2) {
+      tile_step(j, m_cur, m_nxt, st_cur, st_nxt);
+      tile_step(j + 1, m_nxt, m_cur, st_nxt, st_cur);
     }
+    if (j < n) tile_step(j, m_cur, m_nxt, st_cur, st_nxt);
   }
 
   // ---- epilogue
@@ -655,8 +660,7 @@ int attn_launch(const AttnLaunch& a, void* stream) {
   p.ws_o = a.ws_o;
   p.ws_ml = a.ws_ml;
   p.tm_offsets = a.tm_offsets;
-  p.tm_key_tiles = a.tm_key_tiles;
-  p.tm_flags = a.tm_flags;
+  p.tm_desc = a.tm_desc;
   p.mask_tbl = a.mask_tbl;
   p.mt_ky = a.mt_ky;
   p.mt_kx = a.mt_kx;
@@ -668,9 +672,6 @@ int attn_launch(const AttnLaunch& a, void* stream) {
   p.window = a.window;
   p.ntx = (a.gw + kTileW - 1) / kTileW;
   p.ntiles = ((a.gh + kTileH - 1) / kTileH) * p.ntx;
-  p.nkx = (a.gw + kKeyW - 1) / kKeyW;
-  // exact for kt * nkx < 2^32 (kt < 2^21 and nkx <= 1024 on grids up to 8192^2)
-  p.nkx_magic = ((1ull << 32) + (uint64_t)p.nkx - 1) / (uint64_t)p.nkx;
   p.BH = a.B * a.H;
   p.n_text_blocks = (a.n_text + kTextQ - 1) / kTextQ;
   const int nall = (p.N + kChunk - 1) / kChunk;

@@ -19,10 +19,11 @@ namespace {
 thread_local char g_err[512];
 
 struct TileMapDev {
-  void* block = nullptr;  // one allocation holding the three arrays
+  void* block = nullptr;  // one allocation holding the four arrays
   uint32_t* offsets = nullptr;
   uint32_t* key_tiles = nullptr;
   uint16_t* flags = nullptr;
+  uint32_t* desc = nullptr;  // 4 words per entry (tile_map_build_device_launch)
   size_t n_entries = 0;
   hipEvent_t ready = nullptr;  // recorded after the build kernels
   // lane-mask table of partly admitted chunks (null when not built); the host
@@ -64,14 +65,16 @@ int get_tile_map(DevState& ds, int gh, int gw, int r2, int window, hipStream_t s
   const size_t nt = (size_t)g.nty * g.ntx;
   const size_t o_kt = align_up((nt + 1) * 4, 256);
   const size_t o_fl = align_up(o_kt + m.n_entries * 4, 256);
-  const size_t bytes = align_up(o_fl + m.n_entries * 2 + 2, 256);
+  const size_t o_ds = align_up(o_fl + m.n_entries * 2 + 2, 256);
+  const size_t bytes = align_up(o_ds + m.n_entries * 16, 256);
   hipError_t e = hipMalloc(&m.block, bytes);
   if (e != hipSuccess) return set_error(CLEAR_ENOMEM, "tile map allocation (%zu bytes): %s", bytes, hipGetErrorString(e));
   char* b = (char*)m.block;
   m.offsets = (uint32_t*)b;
   m.key_tiles = (uint32_t*)(b + o_kt);
   m.flags = (uint16_t*)(b + o_fl);
-  int rc = tile_map_build_device_launch(g, m.offsets, m.key_tiles, m.flags, stream);
+  m.desc = (uint32_t*)(b + o_ds);
+  int rc = tile_map_build_device_launch(g, m.offsets, m.key_tiles, m.flags, m.desc, stream);
   if (rc) {
     (void)hipFree(m.block);
     return rc;
@@ -248,7 +251,7 @@ int run_forward(const void* q, const void* k, const void* v, void* out, int B, i
   AttnLaunch a;
   memset(&a, 0, sizeof a);
   a.q = q; a.k = k; a.v = v; a.out = out; a.lse = o.lse_out;
-  a.tm_offsets = tm->offsets; a.tm_key_tiles = tm->key_tiles; a.tm_flags = tm->flags;
+  a.tm_offsets = tm->offsets; a.tm_desc = tm->desc;
   a.mask_tbl = tm->mask_tbl; a.mt_ky = tm->mt_ky; a.mt_kx = tm->mt_kx;
   a.B = B; a.H = H; a.d = d; a.n_text = n_text; a.gh = grid_h; a.gw = grid_w; a.r2 = g.r2;
   a.dtype = o.dtype; a.text_splits = splits; a.window = o.window;
@@ -351,7 +354,7 @@ int run_backward(const void* q, const void* k, const void* v, const void* out, c
     a.ws_dk = (float*)((char*)ws + stats_bytes + part_bytes);
     a.ws_dv = (float*)((char*)ws + stats_bytes + 2 * part_bytes);
   }
-  a.tm_offsets = tm->offsets; a.tm_key_tiles = tm->key_tiles; a.tm_flags = tm->flags;
+  a.tm_offsets = tm->offsets; a.tm_desc = tm->desc;
   a.mask_tbl = tm->mask_tbl; a.mt_ky = tm->mt_ky; a.mt_kx = tm->mt_kx;
   a.B = B; a.H = H; a.d = d; a.n_text = n_text; a.gh = grid_h; a.gw = grid_w; a.r2 = g.r2;
   a.dtype = o.dtype; a.text_splits = splits; a.window = o.window;
@@ -448,7 +451,7 @@ extern "C" int clear_tile_map_build_device_ex(int window, int grid_h, int grid_w
     return set_error(CLEAR_ENOMEM, "tile map needs %zu entries (capacity %zu)", *n_entries, cap);
   if (!offsets || (*n_entries && (!key_tiles || !flags)))
     return set_error(CLEAR_EINVAL, "tile map output pointers must not be NULL");
-  rc = tile_map_build_device_launch(g, offsets, key_tiles, flags, stream);
+  rc = tile_map_build_device_launch(g, offsets, key_tiles, flags, nullptr, stream);
   if (rc) return rc;
   if (debug_sync_enabled()) {
     hipError_t e = hipStreamSynchronize((hipStream_t)stream);

@@ -28,8 +28,17 @@ void mask_table_fill(const TileGeom& g, int ky, int kx, uint64_t* out);
 
 // Device builder: enqueue the kernels that fill offsets / key_tiles / flags
 // (capacity already checked against tile_map_count).
+// desc (optional, 4 words per entry): the entry's descriptor for the attention
+// kernels, read through the scalar cache in one load --
+//   [0] token offset of the key tile's first cell from the first image token
+//       (ky * key_h * gw + kx * key_w),
+//   [1] the entry's flags, plus kTileInside when the key tile lies wholly on
+//       the grid,
+//   [2] (ky << 16) | kx, the key tile's row and column,
+//   [3] image tokens from the first cell to the end of the grid.
+constexpr uint32_t kTileInside = 1u << 16;
 int tile_map_build_device_launch(const TileGeom& g, uint32_t* offsets, uint32_t* key_tiles,
-                                 uint16_t* flags, void* stream);
+                                 uint16_t* flags, uint32_t* desc, void* stream);
 
 // Attention launch description (all pointers are device pointers).
 struct AttnLaunch {
@@ -40,9 +49,8 @@ struct AttnLaunch {
   float* lse;                 // optional
   float* ws_o;                // text partials [splits][B*H][n_text][d]   (splits > 1)
   float* ws_ml;               // text partials [splits][B*H][n_text][2]   (splits > 1)
-  const uint32_t* tm_offsets;  // tile map
-  const uint32_t* tm_key_tiles;
-  const uint16_t* tm_flags;
+  const uint32_t* tm_offsets;  // tile map: entry range of each query tile
+  const uint32_t* tm_desc;     //   and each entry's descriptor
   const uint64_t* mask_tbl;   // lane-mask table (NULL: masks computed per element)
   int mt_ky, mt_kx;
   int B, H, d, n_text, gh, gw, r2;
@@ -72,8 +80,7 @@ struct BwdLaunch {
   float* ws_dk;
   float* ws_dv;
   const uint32_t* tm_offsets;
-  const uint32_t* tm_key_tiles;
-  const uint16_t* tm_flags;
+  const uint32_t* tm_desc;
   const uint64_t* mask_tbl;   // lane-mask table (NULL: masks computed per element)
   int mt_ky, mt_kx;
   int B, H, d, n_text, gh, gw, r2;

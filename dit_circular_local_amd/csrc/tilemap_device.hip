@@ -8,7 +8,8 @@
 //      receives the total);
 //   3. one workgroup per query tile: the flags of every candidate key tile, in
 //      blocks of 256 candidates (ascending id), compacted in order with a
-//      wavefront ballot and a prefix over the four wavefronts.
+//      wavefront ballot and a prefix over the four wavefronts; optionally also
+//      each entry's descriptor for the attention kernels (see tile_desc below).
 #include <hip/hip_runtime.h>
 
 #include "clear_internal.h"
@@ -67,7 +68,7 @@ __global__ void __launch_bounds__(kScanThreads) k_scan_offsets(uint32_t* x, int 
 }
 
 __global__ void __launch_bounds__(kThreads) k_tile_fill(TileGeom g, const uint32_t* offsets,
-                                                         uint32_t* key_tiles, uint16_t* flags) {
+                                                         uint32_t* key_tiles, uint16_t* flags, uint32_t* desc) {
   __shared__ uint32_t wcnt[kThreads / 64];
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -98,6 +99,14 @@ __global__ void __launch_bounds__(kThreads) k_tile_fill(TileGeom g, const uint32
       const uint32_t e = base + woff + before;
       key_tiles[e] = (uint32_t)(ky * g.nkx + kx);
       flags[e] = (uint16_t)f;
+      if (desc) {
+        const uint32_t tok = (uint32_t)(ky * g.kh * g.gw + kx * g.kw);
+        const bool inside = ky * g.kh + g.kh <= g.gh && kx * g.kw + g.kw <= g.gw;
+        desc[4 * e + 0] = tok;
+        desc[4 * e + 1] = f | (inside ? kTileInside : 0u);
+        desc[4 * e + 2] = ((uint32_t)ky << 16) | (uint32_t)kx;
+        desc[4 * e + 3] = (uint32_t)(g.gh * g.gw) - tok;
+      }
     }
     base += total;
     __syncthreads();
@@ -107,12 +116,12 @@ __global__ void __launch_bounds__(kThreads) k_tile_fill(TileGeom g, const uint32
 }  // namespace
 
 int tile_map_build_device_launch(const TileGeom& g, uint32_t* offsets, uint32_t* key_tiles,
-                                 uint16_t* flags, void* stream) {
+                                 uint16_t* flags, uint32_t* desc, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   const int nt = g.nty * g.ntx;
   hipLaunchKernelGGL(k_tile_counts, dim3(nt), dim3(kThreads), 0, s, g, offsets);
   hipLaunchKernelGGL(k_scan_offsets, dim3(1), dim3(kScanThreads), 0, s, offsets, nt);
-  hipLaunchKernelGGL(k_tile_fill, dim3(nt), dim3(kThreads), 0, s, g, offsets, key_tiles, flags);
+  hipLaunchKernelGGL(k_tile_fill, dim3(nt), dim3(kThreads), 0, s, g, offsets, key_tiles, flags, desc);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(CLEAR_EHIP, "tile map kernels: %s", hipGetErrorString(e));
   return CLEAR_OK;

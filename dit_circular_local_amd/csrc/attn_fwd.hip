@@ -331,20 +331,21 @@ struct SoftmaxState {
 };
 
 // Online-softmax step of one chunk's masked logits (base 2, lazy reference
-// max): row max over the lane pair, a rescale only when some row's max passes
-// its threshold, probabilities into pr and their sum into L.  Returns true (the
-// same on every lane) when the reference max moved; alpha is then the factor O
-// must be scaled by before this chunk's P.V.  O itself is not touched here, so
-// the caller can skip this step for a chunk the wavefront does not touch.
+// max): a rescale only when some lane's sixteen logits pass their row's
+// threshold (then the row max over the lane pair moves the reference max),
+// probabilities into pr and their sum into L.  Returns true (the same on
+// every lane) when the reference max moved; alpha is then the factor O must
+// be scaled by before this chunk's P.V.  O itself is not touched here, so the
+// caller can skip this step for a chunk the wavefront does not touch.
 template <class E>
 __device__ __forceinline__ bool chunk_softmax(SoftmaxState& sm, f32x16_t& s, float scale_log2,
                                               float inv_scale_log2, typename E::Probs& pr, float& alpha) {
   float mx = s[0];
   for (int i = 1; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, s[i]);
-  mx = max_xor32(mx);
   bool moved = false;
   if (__ballot(mx > sm.T) != 0ull) {
-    const float Mn = fmaxf(sm.M, mx * scale_log2);
+    // both lanes of a row take this branch and agree on the new reference
+    const float Mn = fmaxf(sm.M, max_xor32(mx) * scale_log2);
     alpha = __builtin_amdgcn_exp2f(sm.M - Mn);
     sm.L *= alpha;
     sm.M = Mn;

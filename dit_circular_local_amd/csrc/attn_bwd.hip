@@ -470,24 +470,23 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_bwd_dkd
 
   const BwdPlan<E> plan = make_bwd_plan<E>(wave, lane, p.gw);
   const MaskTable mt{(const_u64_t*)p.mask_tbl, p.mt_ky, p.mt_kx};
-  char* st_cur = smem;
-  char* st_nxt = smem + L::kStageABS;
-  if (n > 0) {
-    ChunkMeta m_cur = chunk_meta(ks, 0);
-    ChunkMeta m_nxt = chunk_meta(ks, n > 1 ? 1 : 0);
-    stage_bwd<E, true>(st_cur, m_cur, 0 < ks.n_dense, wave, p.N, qbase, obase, sbase, plan);
-    for (int j = 0; j < n; ++j) {
-      __syncthreads();
-      if (j + 1 < n) stage_bwd<E, true>(st_nxt, m_nxt, j + 1 < ks.n_dense, wave, p.N, qbase, obase, sbase, plan);
-      const ChunkInfo c = chunk_info(m_cur, j, ks, wave);
-      if (c.active) {
+  const int mt_base = table_base(mt, w.sy0, w.sx0);
+  // one key tile per trip: the paired loop spills this kernel's registers
+  walk_chunks<false>(
+      ks, n, wave, smem, smem + L::kStageABS,
+      [&](char* st, const ChunkMeta& m, bool dense) {
+        stage_bwd<E, true>(st, m, dense, wave, p.N, qbase, obase, sbase, plan);
+      },
+      [&](const ChunkInfo& c, const char* st) {
+        if (!c.active) return;
         f32x16_t s, dp;
-        E::row_mma(st_cur + L::kA, lane, kr, s);
-        if constexpr (E::kOwnInLds) E::row_mma_own(st_cur + L::kB, own_v, lane, dp);
-        else E::row_mma(st_cur + L::kB, lane, vr, dp);
-        if (c.coord && c.inside && mt.tbl != nullptr) mask_from_table(s, mt, c.ky0 - w.sy0, c.kx0 - w.sx0);
+        E::row_mma(st + L::kA, lane, kr, s);
+        if constexpr (E::kOwnInLds) E::row_mma_own(st + L::kB, own_v, lane, dp);
+        else E::row_mma(st + L::kB, lane, vr, dp);
+        if (c.coord && c.inside && mt.tbl != nullptr)
+          apply_lane_masks(s, mt.tbl + ((c.kty * (2 * mt.kx + 1) + c.ktx + mt_base) << 4));
         else mask_chunk(s, c, ks, g, w.cy, w.cx, p.r2);
-        const float* sv = (const float*)(st_cur + L::kStats + 256 * wave);
+        const float* sv = (const float*)(st + L::kStats + 256 * wave);
         for (int a = 0; a < 4; ++a) {
           const f32x4_t l2 = *(const f32x4_t*)(sv + 8 * a + 4 * g);
           const f32x4_t dd = *(const f32x4_t*)(sv + 32 + 8 * a + 4 * g);
@@ -499,17 +498,10 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_bwd_dkd
         }
         typename E::Operand op;
         E::to_operand(s, op);
-        E::tr_mma(st_cur + L::kB, lane, op, dv);
+        E::tr_mma(st + L::kB, lane, op, dv);
         E::to_operand(dp, op);
-        E::tr_mma(st_cur + L::kA, lane, op, dk);
-      }
-      m_cur = m_nxt;
-      m_nxt = chunk_meta(ks, j + 2 < n ? j + 2 : n - 1);
-      char* t = st_cur;
-      st_cur = st_nxt;
-      st_nxt = t;
-    }
-  }
+        E::tr_mma(st + L::kA, lane, op, dk);
+      });
 
   if (!w.valid) return;
   if (w.text) {
@@ -554,21 +546,19 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_bwd_dq_
 
   const BwdPlan<E> plan = make_bwd_plan<E>(wave, lane, p.gw);
   const MaskTable mt{(const_u64_t*)p.mask_tbl, p.mt_ky, p.mt_kx};
-  char* st_cur = smem;
-  char* st_nxt = smem + L::kStageAB;
-  if (n > 0) {
-    ChunkMeta m_cur = chunk_meta(ks, 0);
-    ChunkMeta m_nxt = chunk_meta(ks, n > 1 ? 1 : 0);
-    stage_bwd<E, false>(st_cur, m_cur, 0 < ks.n_dense, wave, p.N, kbase, vbase, nullptr, plan);
-    for (int j = 0; j < n; ++j) {
-      __syncthreads();
-      if (j + 1 < n) stage_bwd<E, false>(st_nxt, m_nxt, j + 1 < ks.n_dense, wave, p.N, kbase, vbase, nullptr, plan);
-      const ChunkInfo c = chunk_info(m_cur, j, ks, wave);
-      if (c.active) {
+  const int mt_base = table_base(mt, w.sy0, w.sx0);
+  walk_chunks<true>(
+      ks, n, wave, smem, smem + L::kStageAB,
+      [&](char* st, const ChunkMeta& m, bool dense) {
+        stage_bwd<E, false>(st, m, dense, wave, p.N, kbase, vbase, nullptr, plan);
+      },
+      [&](const ChunkInfo& c, const char* st) {
+        if (!c.active) return;
         f32x16_t s, dp;
-        E::row_mma(st_cur + L::kA, lane, qr, s);
-        E::row_mma(st_cur + L::kB, lane, dor, dp);
-        if (c.coord && c.inside && mt.tbl != nullptr) mask_from_table(s, mt, c.ky0 - w.sy0, c.kx0 - w.sx0);
+        E::row_mma(st + L::kA, lane, qr, s);
+        E::row_mma(st + L::kB, lane, dor, dp);
+        if (c.coord && c.inside && mt.tbl != nullptr)
+          apply_lane_masks(s, mt.tbl + ((c.kty * (2 * mt.kx + 1) + c.ktx + mt_base) << 4));
         else mask_chunk(s, c, ks, g, w.cy, w.cx, p.r2);
         for (int i = 0; i < 16; ++i) {
           const float pr = __builtin_amdgcn_exp2f(fmaf(s[i], p.scale_log2, -stq.x));
@@ -576,15 +566,8 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_bwd_dq_
         }
         typename E::Operand op;
         E::to_operand(dp, op);
-        E::tr_mma(st_cur + L::kA, lane, op, dq);
-      }
-      m_cur = m_nxt;
-      m_nxt = chunk_meta(ks, j + 2 < n ? j + 2 : n - 1);
-      char* t = st_cur;
-      st_cur = st_nxt;
-      st_nxt = t;
-    }
-  }
+        E::tr_mma(st + L::kA, lane, op, dq);
+      });
 
   if (!w.valid) return;
   if (w.text) {

@@ -142,8 +142,63 @@ __device__ __forceinline__ ChunkInfo tile_chunk_info(const ChunkMeta& m, const K
                    (m.flag & kTileInside) != 0, kChunk, kty, ktx, kty * kKeyH, ktx * kKeyW};
 }
 
-__device__ __forceinline__ ChunkInfo chunk_info(const ChunkMeta& m, int j, const KeySource& ks, int wave) {
-  return j < ks.n_dense ? dense_chunk_info(m, ks) : tile_chunk_info(m, ks, wave);
+// The chunk walk of the attention kernels.  Two LDS stages: after the
+// barrier of iteration j, chunk j is in its stage (the copies were issued in
+// iteration j - 1 and the barrier waits for every wavefront's copies), and
+// every wavefront is done with chunk j - 1, so the copies of chunk j + 1 go to
+// the other stage while chunk j is computed.  The descriptor of chunk j + 2 is
+// fetched in iteration j, so its scalar load is complete when needed.
+//   stage(st, meta, dense) issues the copies of a chunk into stage st;
+//   compute(info, st) computes the chunk held in st.
+// The dense chunks come first (text keys, or all of a text workgroup's
+// chunks; the one after the last may be a key tile).  Each kind of chunk has
+// a loop of its own that carries only its own state and tests, and the key
+// tiles go two per trip so that the stages and the two descriptors in flight
+// keep fixed roles: in tile_step, mc describes chunk jj (in cur), mn chunk
+// jj + 1 (copied to nxt), and mc then receives chunk jj + 2.
+template <bool kPairs = true, class Stage, class Compute>
+__device__ __forceinline__ void walk_chunks(const KeySource& ks, int n, int wave, char* st_cur, char* st_nxt,
+                                            Stage&& stage, Compute&& compute) {
+  if (n <= 0) return;
+  ChunkMeta m_cur = chunk_meta(ks, 0);
+  ChunkMeta m_nxt = chunk_meta(ks, n > 1 ? 1 : 0);
+  stage(st_cur, m_cur, 0 < ks.n_dense);
+  int j = 0;
+  for (; j < ks.n_dense; ++j) {
+    __syncthreads();
+    if (j + 1 < n) stage(st_nxt, m_nxt, j + 1 < ks.n_dense);
+    const ChunkInfo c = dense_chunk_info(m_cur, ks);
+    m_cur = m_nxt;
+    m_nxt = chunk_meta(ks, j + 2 < n ? j + 2 : n - 1);
+    compute(c, (const char*)st_cur);
+    char* t = st_cur;
+    st_cur = st_nxt;
+    st_nxt = t;
+  }
+  auto tile_step = [&](int jj, ChunkMeta& mc, const ChunkMeta& mn, const char* cur, char* nxt) {
+    __syncthreads();
+    if (jj + 1 < n) stage(nxt, mn, false);
+    const ChunkInfo c = tile_chunk_info(mc, ks, wave);
+    mc = tile_chunk_meta(ks, jj + 2 < n ? jj + 2 : n - 1);
+    compute(c, cur);
+  };
+  if constexpr (kPairs) {
+    for (; j + 1 < n; j += 2) {
+      tile_step(j, m_cur, m_nxt, st_cur, st_nxt);
+      tile_step(j + 1, m_nxt, m_cur, st_nxt, st_cur);
+    }
+    if (j < n) tile_step(j, m_cur, m_nxt, st_cur, st_nxt);
+  } else {
+    for (; j < n; ++j) {
+      tile_step(j, m_cur, m_nxt, st_cur, st_nxt);  // m_cur now describes chunk j + 2
+      const ChunkMeta m = m_cur;
+      m_cur = m_nxt;
+      m_nxt = m;
+      char* t = st_cur;
+      st_cur = st_nxt;
+      st_nxt = t;
+    }
+  }
 }
 
 

@@ -473,70 +473,27 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
   const float inv_scale_log2 = 1.0f / p.scale_log2;
   SoftmaxState sm{kMInit, 0.0f, (kMInit + kLazyTau) * inv_scale_log2};
 
-  // ---- chunk loop.  Two LDS stages: after the barrier of iteration j, chunk
-  // j is in stage j % 2 (its direct-to-LDS loads were issued in iteration
-  // j - 1 and are complete: the barrier waits for each wavefront's loads), and
-  // every wavefront is done with chunk j - 1, so the loads of chunk j + 1 can
-  // go to the other stage while chunk j is computed.  The scalar description of
-  // chunk j + 2 is fetched before the barrier, where the wait is paid anyway.
-  const int n = n_chunks;
-  char* st_cur = smem;
-  char* st_nxt = smem + E::kStage;
+  // ---- chunk walk (walk_chunks).  A chunk the wavefront's sub-tile does not
+  // touch skips Q.K and the softmax: its probabilities are zero.  P.V and the
+  // rescale of O stay outside that branch, so O is updated on one path only.
   eng.settle_q();
-  if (n > 0) {
-    ChunkMeta m_cur = chunk_meta(ks, 0);
-    ChunkMeta m_nxt = chunk_meta(ks, n > 1 ? 1 : 0);
-    stage_chunk<E>(st_cur, m_cur, 0 < ks.n_dense, wave, ks, kbase, vbase, plan);
-    // One chunk.  A chunk the wavefront's sub-tile does not touch skips Q.K
-    // and the softmax: its probabilities are zero.  P.V and the rescale of O
-    // stay outside that branch, so O is updated on one path only.
-    auto compute = [&](const ChunkInfo& c, const char* st) {
-      typename E::Probs pr;
-      float alpha = 1.0f;
-      bool moved = false;
-      if (c.active) {
-        f32x16_t sc;
-        chunk_logits(eng, st, lane, sc, c, ks, qy, qx, p.r2, mt, mt_base);
-        moved = chunk_softmax<E>(sm, sc, p.scale_log2, inv_scale_log2, pr, alpha);
-      } else {
-        pr.zero();
-      }
-      if (moved) eng.scale_o(alpha);
-      eng.pv(st, lane, pr);
-    };
-    // The dense chunks come first (the text keys of an image workgroup, all
-    // of a text workgroup's chunks); the one after the last may be a key tile.
-    // Each kind of chunk has a loop of its own, which carries only that
-    // kind's state and tests.
-    int j = 0;
-    for (; j < ks.n_dense; ++j) {
-      __syncthreads();
-      if (j + 1 < n) stage_chunk<E>(st_nxt, m_nxt, j + 1 < ks.n_dense, wave, ks, kbase, vbase, plan);
-      const ChunkInfo c = dense_chunk_info(m_cur, ks);
-      m_cur = m_nxt;
-      m_nxt = chunk_meta(ks, j + 2 < n ? j + 2 : n - 1);
-      compute(c, st_cur);
-      char* t = st_cur;
-      st_cur = st_nxt;
-      st_nxt = t;
-    }
-    // Key tiles, two per trip so that the stages and the two descriptors in
-    // flight keep fixed roles (no copies between iterations): mc describes
-    // chunk jj (staged in cur), mn chunk jj + 1 (to be staged in nxt), and mc
-    // then receives chunk jj + 2.
-    auto tile_step = [&](int jj, ChunkMeta& mc, const ChunkMeta& mn, const char* cur, char* nxt) {
-      __syncthreads();
-      if (jj + 1 < n) stage_chunk<E>(nxt, mn, false, wave, ks, kbase, vbase, plan);
-      const ChunkInfo c = tile_chunk_info(mc, ks, wave);
-      mc = tile_chunk_meta(ks, jj + 2 < n ? jj + 2 : n - 1);
-      compute(c, cur);
-    };
-    for (; j + 1 < n; j += 2) {
-      tile_step(j, m_cur, m_nxt, st_cur, st_nxt);
-      tile_step(j + 1, m_nxt, m_cur, st_nxt, st_cur);
-    }
-    if (j < n) tile_step(j, m_cur, m_nxt, st_cur, st_nxt);
-  }
+  walk_chunks(
+      ks, n_chunks, wave, smem, smem + E::kStage,
+      [&](char* st, const ChunkMeta& m, bool dense) { stage_chunk<E>(st, m, dense, wave, ks, kbase, vbase, plan); },
+      [&](const ChunkInfo& c, const char* st) {
+        typename E::Probs pr;
+        float alpha = 1.0f;
+        bool moved = false;
+        if (c.active) {
+          f32x16_t sc;
+          chunk_logits(eng, st, lane, sc, c, ks, qy, qx, p.r2, mt, mt_base);
+          moved = chunk_softmax<E>(sm, sc, p.scale_log2, inv_scale_log2, pr, alpha);
+        } else {
+          pr.zero();
+        }
+        if (moved) eng.scale_o(alpha);
+        eng.pv(st, lane, pr);
+      });
 
   // ---- epilogue
   const float Lt = sum_xor32(sm.L);

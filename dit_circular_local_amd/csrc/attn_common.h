@@ -155,8 +155,11 @@ __device__ __forceinline__ ChunkInfo tile_chunk_info(const ChunkMeta& m, const K
 // a loop of its own that carries only its own state and tests, and the key
 // tiles go two per trip so that the stages and the two descriptors in flight
 // keep fixed roles: in tile_step, mc describes chunk jj (in cur), mn chunk
-// jj + 1 (copied to nxt), and mc then receives chunk jj + 2.
-template <bool kPairs = true, class Stage, class Compute>
+// jj + 1 (copied to nxt), and mc then receives chunk jj + 2.  Walk::kSplit
+// keeps one key tile per trip (less code, where registers are scarce).
+enum class Walk { kSplit, kSplitPairs };
+
+template <Walk kWalk = Walk::kSplitPairs, class Stage, class Compute>
 __device__ __forceinline__ void walk_chunks(const KeySource& ks, int n, int wave, char* st_cur, char* st_nxt,
                                             Stage&& stage, Compute&& compute) {
   if (n <= 0) return;
@@ -182,7 +185,7 @@ __device__ __forceinline__ void walk_chunks(const KeySource& ks, int n, int wave
     mc = tile_chunk_meta(ks, jj + 2 < n ? jj + 2 : n - 1);
     compute(c, cur);
   };
-  if constexpr (kPairs) {
+  if constexpr (kWalk == Walk::kSplitPairs) {
     for (; j + 1 < n; j += 2) {
       tile_step(j, m_cur, m_nxt, st_cur, st_nxt);
       tile_step(j + 1, m_nxt, m_cur, st_nxt, st_cur);

@@ -12,8 +12,9 @@
 //    chunks of 32: first the text keys, then the 4 x 8 cell key tiles the tile
 //    map lists for the query tile.  A wavefront skips key tiles its sub-tile does
 //    not touch and applies the per-element circular mask only to key tiles it
-//    does not fully admit (one select per element, its lane mask read from a
-//    small table indexed by the tile's offset from the sub-tile);
+//    does not fully admit: the mask (0 or -inf per element, from a small table
+//    of lane masks indexed by the tile's offset from the sub-tile) is the Q.K
+//    product's initial accumulator;
 //  * text workgroups: 128 text queries against a contiguous range of all keys
 //    (the range is one of `splits` parts; partial results are merged exactly by
 //    log-sum-exp in a second kernel when splits > 1).
@@ -22,16 +23,17 @@
 //    S^T[key][query] = K[key][:] . Q[query][:]          A = K (LDS), B = Q^T (VGPRs)
 //    O^T[d][query]  += V^T[d][key] . P^T[key][query]    A = V^T (LDS), B = P^T (VGPRs)
 // With the 32x32 accumulator layout, lane l holds 16 keys of query l % 32, so
-// the softmax row statistics are per lane (plus one exchange with lane l ^ 32)
-// and the rescaling of O^T is per lane.  bf16 uses v_mfma_f32_32x32x16_bf16 with
+// the softmax row statistics are per lane (plus an exchange with lane l ^ 32
+// when the reference max moves) and the rescaling of O^T is per lane.  bf16 uses v_mfma_f32_32x32x16_bf16 with
 // V^T read from row-major V by the LDS transpose load ds_read_b64_tr_b16; fp32
 // uses v_mfma_f32_32x32x2_f32.
 //
-// Pipeline: two LDS stages and one workgroup barrier per chunk.  Each chunk
-// goes from global memory straight into LDS (direct-to-LDS buffer loads issued
-// by all four wavefronts) one iteration before it is consumed, so the copy of
-// chunk j + 1 overlaps the computation on chunk j.  Three wavefronts per SIMD
-// (bf16) hide the remaining latency.
+// Pipeline (walk_chunks): two LDS stages and one workgroup barrier per chunk.
+// Each chunk goes from global memory straight into LDS (direct-to-LDS buffer
+// loads issued by all four wavefronts) one iteration before it is consumed, so
+// the copy of chunk j + 1 overlaps the computation on chunk j; each key tile's
+// 16-byte tile-map descriptor arrives by one scalar load two chunks ahead.
+// Three wavefronts per SIMD (bf16) hide the remaining latency.
 //
 // Online softmax in base 2 with a lazily updated reference max: p = 2^(s*c - M)
 // with c = log2(e)/sqrt(d); M is raised only when a row max exceeds M + 8, so

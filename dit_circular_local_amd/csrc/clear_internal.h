@@ -34,7 +34,8 @@ void mask_table_fill(const TileGeom& g, int ky, int kx, uint64_t* out);
 //       (ky * key_h * gw + kx * key_w),
 //   [1] the entry's flags, plus kTileInside when the key tile lies wholly on
 //       the grid,
-//   [2] (ky << 16) | kx, the key tile's row and column,
+//   [2] (ky << 16) | kx, the key tile's row and column (16 bits each suffice:
+//       grid sides are at most CLEAR_MAX_GRID),
 //   [3] image tokens from the first cell to the end of the grid.
 constexpr uint32_t kTileInside = 1u << 16;
 int tile_map_build_device_launch(const TileGeom& g, uint32_t* offsets, uint32_t* key_tiles,

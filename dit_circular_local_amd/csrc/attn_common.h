@@ -205,15 +205,6 @@ __device__ __forceinline__ void walk_chunks(const KeySource& ks, int n, int wave
 }
 
 
-// The window mask of one chunk, in place on 32x32 accumulator values s whose
-// rows are the chunk's 32 positions (register i of lane group g is position
-// acc_row(i, g)) and whose column is the lane's own cell (cy, cx).  A dense
-// chunk masks positions >= tail; a key-tile chunk that is not wholly admitted
-// masks by coordinates: position 8a + c is cell (ky0 + a, kx0 + c), admitted
-// iff dx^2 <= lim[a], lim = r2 - dy^2 (circle) or lim = dy^2 <= r2 ? r2 : -1
-// (square), with the chunk's cell on the grid.  The distance is symmetric, so
-// the same code serves a query column against key rows and a key column
-// against query rows.
 // The lane-mask table of partly admitted chunks (built on the host next to
 // the tile map): for a chunk tile at offset (dy, dx) = (4 iy, 8 ix) from the
 // wavefront's sub-tile, word i has bit l set iff register i of lane l is
@@ -230,10 +221,6 @@ __device__ __forceinline__ void apply_lane_masks(f32x16_t& s, const_u64_t* w) {
   for (int i = 0; i < 16; ++i) s[i] = __builtin_amdgcn_inverse_ballot_w64(w[i]) ? s[i] : -__builtin_inff();
 }
 
-__device__ __forceinline__ void mask_from_table(f32x16_t& s, const MaskTable& mt, int dy, int dx) {
-  apply_lane_masks(s, mt.tbl + ((((dy >> 2) + mt.ky) * (2 * mt.kx + 1) + (dx >> 3) + mt.kx) << 4));
-}
-
 // Table row of a wavefront whose sub-tile starts at cell (sy0, sx0), a
 // multiple of (4, 8): the words of key tile (kty, ktx) start at entry
 // kty * (2 kx + 1) + ktx + table_base(mt, sy0, sx0).
@@ -241,6 +228,15 @@ __device__ __forceinline__ int table_base(const MaskTable& mt, int sy0, int sx0)
   return (mt.ky - (sy0 >> 2)) * (2 * mt.kx + 1) + mt.kx - (sx0 >> 3);
 }
 
+// The window mask of one chunk, in place on 32x32 accumulator values s whose
+// rows are the chunk's 32 positions (register i of lane group g is position
+// acc_row(i, g)) and whose column is the lane's own cell (cy, cx).  A dense
+// chunk masks positions >= tail; a key-tile chunk that is not wholly admitted
+// masks by coordinates: position 8a + c is cell (ky0 + a, kx0 + c), admitted
+// iff dx^2 <= lim[a], lim = r2 - dy^2 (circle) or lim = dy^2 <= r2 ? r2 : -1
+// (square), with the chunk's cell on the grid.  The distance is symmetric, so
+// the same code serves a query column against key rows and a key column
+// against query rows.
 __device__ __forceinline__ void mask_chunk(f32x16_t& s, const ChunkInfo& c, const KeySource& ks, int g,
                                            int cy, int cx, int r2) {
   if (c.tail < 32) {

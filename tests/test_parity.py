@@ -208,3 +208,23 @@ def test_flux_8192_sampled_rows(r):
     assert torch.isfinite(out).all()
     del q, k, v, out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("window", ["circle", "square"])
+def test_radius_beyond_the_mask_table(window):
+    """Radius 257 on a 262 x 21 grid + 8 text tokens, fp32, d 64: no lane-mask
+    table is built above radius 256 (the grid's diagonal still exceeds it, so r2
+    is not clamped), and partly admitted key tiles wholly on the grid take their
+    masks from the per-element computation (rows more than 257 apart are cut).
+    Sampled 8 x 8 blocks (top, bottom, ragged corners, middle) and text rows
+    against the oracle row by row at 1e-5."""
+    n_text, gh, gw, d, r2 = 8, 262, 21, 64, 257 * 257
+    q, k, v = make_qkv(1, 1, n_text, gh, gw, d, "fp32", 7, scale=1.0 / math.sqrt(d), device="cuda")
+    out = ca.fwd(q, k, v, n_text, gh, gw, r2=r2, window=window)
+    torch.cuda.synchronize()
+    blocks = [(0, 0), (0, 13), (254, 0), (256, 16), (128, 8), (4, 8), (259, 5)]
+    rows = [0, n_text - 1] + [n_text + (y0 + y) * gw + x0 + x for y0, x0 in blocks
+                              for y in range(8) for x in range(8) if y0 + y < gh and x0 + x < gw]
+    ref, _ = attention_rows(_np(q[0, 0]), _np(k[0, 0]), _np(v[0, 0]), n_text, gh, gw, r2, rows, window=window)
+    err = np.abs(_np(out[0, 0, rows]) - ref).max()
+    assert err <= TOL["fp32"], f"{window} r2={r2}: max-abs {err:.3e}"

@@ -169,3 +169,28 @@ def test_bwd_rejects_bad_arguments():
     with pytest.raises(ca.ClearError) as e:
         ca.bwd(q, k, v, out, do, lse, 8, 4, 4, radius=1, grads=(q, torch.empty_like(q), torch.empty_like(q)))
     assert e.value.code == ca.CLEAR_EINVAL and "overlap" in ca.last_error()
+
+
+@pytest.mark.parametrize("window", ["circle", "square"])
+def test_radius_beyond_the_mask_table(window):
+    """Radius 257 on a 262 x 21 grid + 8 text tokens, fp32, d 64 (no lane-mask
+    table above radius 256; the grid's diagonal exceeds it, so r2 is not
+    clamped): dq of sampled query blocks and text rows, dk and dv of sampled
+    keys, against the oracle at 1e-5."""
+    n_text, gh, gw, d, r2 = 8, 262, 21, 64, 257 * 257
+    q, k, v, do = _inputs("fp32", 1, 1, n_text, gh, gw, d, 8)
+    dq, dk, dv = _gpu_grads(q, k, v, do, n_text, gh, gw, r2, window)
+    qh, kh, vh, dh = (_np(t[0, 0]) for t in (q, k, v, do))
+    blocks = [(0, 0), (32, 2), (16, 1)]  # 8 x 8 blocks: corner, the last (ragged) block, an interior one
+    text_rows = [0, n_text - 1]
+    ref_dq, _, _ = attention_backward_head(qh, kh, vh, dh, n_text, gh, gw, r2, text_rows=text_rows,
+                                           blocks=blocks, window=window)
+    rows = text_rows + [n_text + (8 * by + y) * gw + 8 * bx + x for by, bx in blocks
+                        for y in range(8) for x in range(8) if 8 * by + y < gh and 8 * bx + x < gw]
+    err = np.abs(_np(dq[0, 0, rows]) - ref_dq[rows]).max()
+    assert err <= FP32_TOL, f"dq {window}: {err:.3e}"
+    keys = [0, n_text + 0, n_text + 130 * gw + 10, n_text + gh * gw - 1, n_text + 259 * gw + 3]
+    ref_dk, ref_dv = key_grads(qh, kh, vh, dh, n_text, gh, gw, r2, keys, window=window)
+    for name, g, r in (("dk", dk, ref_dk), ("dv", dv, ref_dv)):
+        err = np.abs(_np(g[0, 0, keys]) - r).max()
+        assert err <= FP32_TOL, f"{name} {window}: {err:.3e}"

@@ -166,14 +166,25 @@ __device__ __forceinline__ void walk_chunks(const KeySource& ks, int n, int wave
   ChunkMeta m_cur = chunk_meta(ks, 0);
   ChunkMeta m_nxt = chunk_meta(ks, n > 1 ? 1 : 0);
   stage(st_cur, m_cur, 0 < ks.n_dense);
-  int j = 0;
-  for (; j < ks.n_dense; ++j) {
+  auto dense_step = [&](int jj, ChunkMeta& mc, const ChunkMeta& mn, const char* cur, char* nxt) {
     __syncthreads();
-    if (j + 1 < n) stage(st_nxt, m_nxt, j + 1 < ks.n_dense);
-    const ChunkInfo c = dense_chunk_info(m_cur, ks);
+    if (jj + 1 < n) stage(nxt, mn, jj + 1 < ks.n_dense);
+    const ChunkInfo c = dense_chunk_info(mc, ks);
+    mc = chunk_meta(ks, jj + 2 < n ? jj + 2 : n - 1);
+    compute(c, cur);
+  };
+  int j = 0;
+  if constexpr (kWalk == Walk::kSplitPairs) {
+    for (; j + 1 < ks.n_dense; j += 2) {
+      dense_step(j, m_cur, m_nxt, st_cur, st_nxt);
+      dense_step(j + 1, m_nxt, m_cur, st_nxt, st_cur);
+    }
+  }
+  for (; j < ks.n_dense; ++j) {
+    dense_step(j, m_cur, m_nxt, st_cur, st_nxt);  // m_cur now describes chunk j + 2
+    const ChunkMeta m = m_cur;
     m_cur = m_nxt;
-    m_nxt = chunk_meta(ks, j + 2 < n ? j + 2 : n - 1);
-    compute(c, (const char*)st_cur);
+    m_nxt = m;
     char* t = st_cur;
     st_cur = st_nxt;
     st_nxt = t;

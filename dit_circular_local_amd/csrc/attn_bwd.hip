@@ -18,8 +18,9 @@
 //  2. dK/dV, key-centred.  Image workgroups own a 16 x 8 cell key tile, each
 //     wavefront a 4 x 8 key sub-tile (32 keys) with its K rows in registers
 //     and its V rows in registers (fp32) or in an LDS region of its own (bf16,
-//     for the register budget of two wavefronts per SIMD).  Queries stream through LDS in chunks of 32: the text queries,
-//     then the 4 x 8 query tiles the tile map lists for the tile.  The window is
+//     for the register budget of two wavefronts per SIMD).  Queries stream
+//     through LDS in chunks of 32: the text queries, then the 4 x 8 query
+//     tiles the tile map lists for the tile.  The window is
 //     symmetric and query and key tiles have the same shapes, so the map built
 //     for query tiles (key tiles per tile, touched/full flags per sub-tile)
 //     reads unchanged for key tiles.  Text-key workgroups take 128 text keys

@@ -258,9 +258,10 @@ struct F32 {
 // 64 * block + l); the K region holds key rows at a pitch of kSlotsK slots, the
 // V region at kSlotsV, so a slot is either piece p of row r or row padding.
 // Block b of a region goes to wavefront b % 4 (regions are padded to a
-// multiple of four blocks, so every wavefront issues the same loads).  Each lane keeps, per block it
-// fills, the byte offset of its piece from the chunk's first key: one for a
-// dense token range and one for a key tile (rows 8 apart on the grid).
+// multiple of four blocks, so every wavefront issues the same loads).  Each
+// lane keeps, per block it fills, the byte offset of its piece from the
+// chunk's first key: one for a dense token range and one for a key tile (rows
+// 8 apart on the grid).
 // Padding slots get an offset past any buffer bound and load zeros.
 template <class E>
 struct DmaPlan {

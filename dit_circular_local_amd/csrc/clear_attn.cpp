@@ -68,7 +68,8 @@ int get_tile_map(DevState& ds, int gh, int gw, int r2, int window, hipStream_t s
   const size_t o_ds = align_up(o_fl + m.n_entries * 2 + 2, 256);
   const size_t bytes = align_up(o_ds + m.n_entries * 16, 256);
   hipError_t e = hipMalloc(&m.block, bytes);
-  if (e != hipSuccess) return set_error(CLEAR_ENOMEM, "tile map allocation (%zu bytes): %s", bytes, hipGetErrorString(e));
+  if (e != hipSuccess)
+    return set_error(CLEAR_ENOMEM, "tile map allocation (%zu bytes): %s", bytes, hipGetErrorString(e));
   char* b = (char*)m.block;
   m.offsets = (uint32_t*)b;
   m.key_tiles = (uint32_t*)(b + o_kt);

@@ -319,12 +319,12 @@ __device__ __forceinline__ void stage_own(char* region, const char* head, int fi
 }
 
 template <class E, bool STATS>
-__device__ __forceinline__ void stage_bwd(char* st, const ChunkMeta& m, bool dense, int wave, int n_tok,
+__device__ __forceinline__ void stage_bwd(char* st, const ChunkMeta& m, bool dense, int wave,
                                           const char* abase, const char* bbase, const float* sbase,
                                           const BwdPlan<E>& pl) {
   const size_t base = (size_t)m.tok0 * E::kRowBytes;
-  const size_t left = (size_t)(n_tok - m.tok0) * E::kRowBytes;
-  const uint32_t bytes = left < 0x7fffffffu ? (uint32_t)left : 0x7fffffffu;
+  constexpr int kMaxLeft = 0x7fffffff / E::kRowBytes;  // a resource covers < 2 GB
+  const uint32_t bytes = (uint32_t)(m.left < kMaxLeft ? m.left : kMaxLeft) * E::kRowBytes;
   const __amdgpu_buffer_rsrc_t ra = byte_rsrc(abase + base, bytes), rb = byte_rsrc(bbase + base, bytes);
   char* sa = st + BwdLayout<E>::kA + 1024 * wave;
   char* sb = st + BwdLayout<E>::kB + 1024 * wave;
@@ -334,9 +334,8 @@ __device__ __forceinline__ void stage_bwd(char* st, const ChunkMeta& m, bool den
   for (int i = 0; i < BwdPlan<E>::kPerWave; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(sb + 1024 * kWaves * i), 16, (int)off[i], 0, 0, 0);
   if constexpr (STATS) {
-    const size_t sleft = (size_t)(n_tok - m.tok0) * 8;
-    const __amdgpu_buffer_rsrc_t rs =
-        byte_rsrc((const char*)(sbase + (size_t)m.tok0 * 2), sleft < 0x7fffffffu ? (uint32_t)sleft : 0x7fffffffu);
+    const __amdgpu_buffer_rsrc_t rs = byte_rsrc((const char*)(sbase + (size_t)m.tok0 * 2),
+                                                (uint32_t)(m.left < 0x0fffffff ? m.left : 0x0fffffff) * 8);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(st + BwdLayout<E>::kStats + 256 * wave), 4,
                                              (int)(dense ? pl.st_dense : pl.st_tile), 0, 0, 0);
   }
@@ -476,7 +475,7 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_bwd_dkd
   walk_chunks<Walk::kSplit>(
       ks, n, wave, smem, smem + L::kStageABS,
       [&](char* st, const ChunkMeta& m, bool dense) {
-        stage_bwd<E, true>(st, m, dense, wave, p.N, qbase, obase, sbase, plan);
+        stage_bwd<E, true>(st, m, dense, wave, qbase, obase, sbase, plan);
       },
       [&](const ChunkInfo& c, const char* st) {
         if (!c.active) return;
@@ -551,7 +550,7 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_bwd_dq_
   walk_chunks<Walk::kSplitPairs>(
       ks, n, wave, smem, smem + L::kStageAB,
       [&](char* st, const ChunkMeta& m, bool dense) {
-        stage_bwd<E, false>(st, m, dense, wave, p.N, kbase, vbase, nullptr, plan);
+        stage_bwd<E, false>(st, m, dense, wave, kbase, vbase, nullptr, plan);
       },
       [&](const ChunkInfo& c, const char* st) {
         if (!c.active) return;

@@ -228,3 +228,44 @@ def test_radius_beyond_the_mask_table(window):
     ref, _ = attention_rows(_np(q[0, 0]), _np(k[0, 0]), _np(v[0, 0]), n_text, gh, gw, r2, rows, window=window)
     err = np.abs(_np(out[0, 0, rows]) - ref).max()
     assert err <= TOL["fp32"], f"{window} r2={r2}: max-abs {err:.3e}"
+
+
+def test_host_threads_share_the_tile_map_cache():
+    """Eight host threads call the forward at once on one stream (ctypes drops
+    the GIL for the call), building six tile maps concurrently in a cold cache;
+    every output equals a single-threaded run bit for bit (the cache is guarded
+    by the library's mutex; calls on one stream are ordered)."""
+    import threading
+
+    configs = [(16, 16, 16), (19, 13, 9), (24, 40, 25), (16, 16, 4), (33, 7, 2), (9, 30, 64)]
+    n_text, d = 8, 64
+    inputs = [make_qkv(1, 2, n_text, gh, gw, d, "fp32", 40 + i, scale=1.0 / math.sqrt(d), device="cuda")
+              for i, (gh, gw, _) in enumerate(configs)]
+    ca.release_cache()
+    ref = [ca.fwd(q, k, v, n_text, gh, gw, r2=r2) for (q, k, v), (gh, gw, r2) in zip(inputs, configs)]
+    torch.cuda.synchronize()
+    ca.release_cache()
+    jobs = [i % len(configs) for i in range(2 * len(configs))]
+    outs = [torch.empty_like(inputs[i][0]) for i in jobs]
+    errors = []
+    stream = torch.cuda.current_stream()
+
+    def worker(t):
+        try:
+            with torch.cuda.stream(stream):
+                for n in range(t, len(jobs), 8):
+                    i = jobs[n]
+                    (q, k, v), (gh, gw, r2) = inputs[i], configs[i]
+                    ca.fwd(q, k, v, n_text, gh, gw, r2=r2, out=outs[n])
+        except Exception as e:  # noqa: BLE001 - reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for n, i in enumerate(jobs):
+        assert torch.equal(outs[n], ref[i]), f"job {n} (config {configs[i]})"

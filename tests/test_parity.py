@@ -269,3 +269,22 @@ def test_host_threads_share_the_tile_map_cache():
     assert not errors, errors
     for n, i in enumerate(jobs):
         assert torch.equal(outs[n], ref[i]), f"job {n} (config {configs[i]})"
+
+
+@pytest.mark.parametrize("gh,gw", [(ca.MAX_GRID, 3), (5, ca.MAX_GRID)])
+@pytest.mark.parametrize("r2", [9, 10 ** 6])
+def test_maximum_grid_side(gh, gw, r2):
+    """Grid sides at the largest accepted value (CLEAR_MAX_GRID), fp32, d 64,
+    4 text tokens; r2 = 10^6 exceeds the mask table's radius (no table).
+    Sampled rows (both ends of the long side, the middle, text rows) against
+    the oracle at 1e-5."""
+    n_text, d = 4, 64
+    q, k, v = make_qkv(1, 1, n_text, gh, gw, d, "fp32", 50, scale=1.0 / math.sqrt(d), device="cuda")
+    out = ca.fwd(q, k, v, n_text, gh, gw, r2=r2)
+    torch.cuda.synchronize()
+    cells = [(0, 0), (gh - 1, gw - 1), (gh // 2, gw // 2), (gh - 1, 0), (0, gw - 1), (gh // 3, gw // 3)]
+    rows = [0, n_text - 1] + [n_text + y * gw + x for y, x in cells]
+    ref, _ = attention_rows(_np(q[0, 0]), _np(k[0, 0]), _np(v[0, 0]), n_text, gh, gw, r2, rows)
+    err = np.abs(_np(out[0, 0, rows]) - ref).max()
+    assert err <= TOL["fp32"], f"{gh}x{gw} r2={r2}: max-abs {err:.3e}"
+    assert torch.isfinite(out).all()

@@ -288,3 +288,11 @@ def test_maximum_grid_side(gh, gw, r2):
     err = np.abs(_np(out[0, 0, rows]) - ref).max()
     assert err <= TOL["fp32"], f"{gh}x{gw} r2={r2}: max-abs {err:.3e}"
     assert torch.isfinite(out).all()
+
+
+@pytest.mark.parametrize("n_text,gh,gw", [(3, 1, 1), (0, 1, 1), (5, 1, 7), (0, 9, 1), (2, 1, 40)])
+@pytest.mark.parametrize("r2", [0, 1, 50])
+def test_degenerate_grids(n_text, gh, gw, r2):
+    """One image token, one row, one column (with and without text), fp32,
+    every output element and the LSE against the oracle."""
+    _check_full("fp32", 1, 2, n_text, gh, gw, 64, r2)

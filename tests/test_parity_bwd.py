@@ -194,3 +194,11 @@ def test_radius_beyond_the_mask_table(window):
     for name, g, r in (("dk", dk, ref_dk), ("dv", dv, ref_dv)):
         err = np.abs(_np(g[0, 0, keys]) - r).max()
         assert err <= FP32_TOL, f"{name} {window}: {err:.3e}"
+
+
+@pytest.mark.parametrize("n_text,gh,gw", [(3, 1, 1), (0, 1, 1), (5, 1, 7), (0, 9, 1), (2, 1, 40)])
+@pytest.mark.parametrize("r2", [0, 1, 50])
+def test_degenerate_grids(n_text, gh, gw, r2):
+    """One image token, one row, one column (with and without text), fp32,
+    every gradient element against the oracle."""
+    _check("fp32", 1, 2, n_text, gh, gw, 64, r2)

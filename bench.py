@@ -64,9 +64,9 @@ def admitted_pairs(n_text: int, gh: int, gw: int, r2: int, window: str = "circle
 def computed_pairs(ca, n_text: int, gh: int, gw: int, r2: int, window: str = "circle") -> float:
     """Query-key products the kernels evaluate per head, tile waste included, in
     pair units (one pair = Q.K plus P.V work, 4d flops).  Per 32-query x 32-key
-    chunk of a wavefront: Q.K runs for text chunks and for listed key tiles its
-    sub-tile touches; P.V runs for every chunk (untouched ones with zero
-    probabilities).  Text workgroups run every chunk of all N keys."""
+    chunk of a wavefront: Q.K and P.V run for text chunks and for the listed key
+    tiles its sub-tile touches (masked pairs inside such a chunk included);
+    untouched ones are skipped.  Text workgroups run every chunk of all N keys."""
     import numpy as np
 
     tm = ca.tile_map_build(gh, gw, r2, window=window)
@@ -77,11 +77,9 @@ def computed_pairs(ca, n_text: int, gh: int, gw: int, r2: int, window: str = "ci
     per_chunk = ca.CHUNK * 32
     text_chunks = -(-n_text // ca.CHUNK)
     dense = ntiles * nsub * text_chunks
-    qk = dense + touched
-    pv = dense + len(f) * nsub
     n = n_text + gh * gw
     text_rows = -(-n_text // 128) * 4 * (-(-n // ca.CHUNK))
-    return (0.5 * (qk + pv) + text_rows) * per_chunk
+    return (dense + touched + text_rows) * per_chunk
 
 
 # sources the forward attention kernel is compiled from (its traffic figures

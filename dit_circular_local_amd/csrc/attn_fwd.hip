@@ -135,7 +135,6 @@ struct Bf16 {
   // operand t) and their sum, taken over the rounded values P.V uses.
   struct Probs {
     bf16x8_t b[2];
-    __device__ void zero() { b[0] = b[1] = bf16x8_t{}; }
   };
   __device__ static void probs(const f32x16_t& e, Probs& pr, float& l) {
     const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -233,7 +232,6 @@ struct F32 {
   }
   struct Probs {
     f32x16_t p;
-    __device__ void zero() { p = f32x16_t{}; }
   };
   __device__ static void probs(const f32x16_t& e, Probs& pr, float& l) {
     for (int i = 0; i < 16; ++i) l += e[i];
@@ -477,24 +475,19 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
   SoftmaxState sm{kMInit, 0.0f, (kMInit + kLazyTau) * inv_scale_log2};
 
   // ---- chunk walk (walk_chunks).  A chunk the wavefront's sub-tile does not
-  // touch skips Q.K and the softmax: its probabilities are zero.  P.V and the
-  // rescale of O stay outside that branch, so O is updated on one path only.
+  // touch contributes nothing to its rows: the wavefront skips its products
+  // and softmax and only takes part in the copies and barriers.
   eng.settle_q();
   walk_chunks(
       ks, n_chunks, wave, smem, smem + E::kStage,
       [&](char* st, const ChunkMeta& m, bool dense) { stage_chunk<E>(st, m, dense, wave, ks, kbase, vbase, plan); },
       [&](const ChunkInfo& c, const char* st) {
+        if (!c.active) return;
         typename E::Probs pr;
         float alpha = 1.0f;
-        bool moved = false;
-        if (c.active) {
-          f32x16_t sc;
-          chunk_logits(eng, st, lane, sc, c, ks, qy, qx, p.r2, mt, mt_base);
-          moved = chunk_softmax<E>(sm, sc, p.scale_log2, inv_scale_log2, pr, alpha);
-        } else {
-          pr.zero();
-        }
-        if (moved) eng.scale_o(alpha);
+        f32x16_t sc;
+        chunk_logits(eng, st, lane, sc, c, ks, qy, qx, p.r2, mt, mt_base);
+        if (chunk_softmax<E>(sm, sc, p.scale_log2, inv_scale_log2, pr, alpha)) eng.scale_o(alpha);
         eng.pv(st, lane, pr);
       });
 

@@ -33,3 +33,13 @@ def test_square_admitted_pairs_match_oracle(n_text, gh, gw, r2):
     if (n_text + gh * gw) <= 200:
         assert bench.admitted_pairs(n_text, gh, gw, r2, "square") == \
             pair_count_bruteforce(n_text, gh, gw, r2, "square")
+
+
+@pytest.mark.parametrize("window", ["circle", "square"])
+@pytest.mark.parametrize("n_text,gh,gw,r2", [(512, 64, 64, 256), (7, 9, 13, 5), (0, 19, 13, 9), (40, 4, 4, 0)])
+def test_computed_work_covers_every_admitted_pair(n_text, gh, gw, r2, window):
+    """The kernels' chunk count (tile waste included) never falls below the
+    admitted pairs: every admitted pair lies in a chunk its wavefront computes."""
+    import dit_circular_local_amd as ca
+
+    assert bench.computed_pairs(ca, n_text, gh, gw, r2, window) >= bench.admitted_pairs(n_text, gh, gw, r2, window)

@@ -62,6 +62,11 @@ int get_tile_map(DevState& ds, int gh, int gw, int r2, int window, hipStream_t s
   }
   TileMapDev m;
   m.n_entries = tile_map_count(g);
+  if (m.n_entries > (size_t)kMaxKernelEntries)
+    return set_error(CLEAR_ENOTSUP,
+                     "the tile map of a %d x %d grid at r2 %d holds %zu key tiles; the attention kernels "
+                     "index at most %d",
+                     gh, gw, g.r2, m.n_entries, kMaxKernelEntries);
   const size_t nt = (size_t)g.nty * g.ntx;
   const size_t o_kt = align_up((nt + 1) * 4, 256);
   const size_t o_fl = align_up(o_kt + m.n_entries * 4, 256);
@@ -222,7 +227,7 @@ int run_forward(const void* q, const void* k, const void* v, void* out, int B, i
       return set_error(CLEAR_EINVAL, "text partial buffers must be 4-byte aligned");
   }
   const long long N = (long long)n_text + (long long)grid_h * grid_w;
-  if (N > 0x7fffffffLL) return set_error(CLEAR_EINVAL, "sequence too long");
+  if (N > kMaxTokens) return set_error(CLEAR_EINVAL, "sequence too long (N = %lld; at most %lld)", N, kMaxTokens);
   const size_t elem = o.dtype == CLEAR_BF16 ? 2 : 4;
   const size_t bytes = (size_t)B * H * (size_t)N * d * elem;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15)
@@ -303,7 +308,7 @@ int run_backward(const void* q, const void* k, const void* v, const void* out, c
     return set_error(CLEAR_EINVAL, "text_splits must be in 0..64 (got %d)", o.text_splits);
   if (o.lse_out) return set_error(CLEAR_EINVAL, "lse_out is a forward output; pass NULL to the backward");
   const long long N = (long long)n_text + (long long)grid_h * grid_w;
-  if (N > 0x7fffffffLL) return set_error(CLEAR_EINVAL, "sequence too long");
+  if (N > kMaxTokens) return set_error(CLEAR_EINVAL, "sequence too long (N = %lld; at most %lld)", N, kMaxTokens);
   const size_t elem = o.dtype == CLEAR_BF16 ? 2 : 4;
   const size_t bytes = (size_t)B * H * (size_t)N * d * elem;
   const size_t lse_bytes = (size_t)B * H * (size_t)N * 4;
@@ -413,7 +418,7 @@ extern "C" int clear_text_merge(const float* part_o, const float* part_ml, int n
   if (dtype != CLEAR_BF16 && dtype != CLEAR_FP32)
     return set_error(CLEAR_EINVAL, "dtype must be CLEAR_BF16 or CLEAR_FP32 (got %d)", dtype);
   const long long N = (long long)n_text + (long long)grid_h * grid_w;
-  if (N > 0x7fffffffLL) return set_error(CLEAR_EINVAL, "sequence too long");
+  if (N > kMaxTokens) return set_error(CLEAR_EINVAL, "sequence too long (N = %lld; at most %lld)", N, kMaxTokens);
   int rc = text_merge_launch(part_o, part_ml, nparts, mode, out, lse_out, B * H, n_text, (int)N, d,
                              dtype, stream);
   if (rc) return rc;
@@ -448,6 +453,8 @@ extern "C" int clear_tile_map_build_device_ex(int window, int grid_h, int grid_w
   if (!n_entries) return set_error(CLEAR_EINVAL, "n_entries must not be NULL");
   TileGeom g = make_geom(grid_h, grid_w, r2_max, tile_h, tile_w, sub_h, sub_w, key_h, key_w, window);
   *n_entries = tile_map_count(g);
+  rc = tile_map_check_entries(*n_entries);
+  if (rc) return rc;
   if (*n_entries > cap)
     return set_error(CLEAR_ENOMEM, "tile map needs %zu entries (capacity %zu)", *n_entries, cap);
   if (!offsets || (*n_entries && (!key_tiles || !flags)))

@@ -16,8 +16,18 @@ bool debug_sync_enabled();
 
 int tile_map_validate(int gh, int gw, int r2, int th, int tw, int sh, int sw, int kh, int kw);
 size_t tile_map_count(const TileGeom& g);
-void tile_map_fill_host(const TileGeom& g, uint32_t* offsets, uint32_t* key_tiles,
-                        uint16_t* flags);
+// CLEAR_ENOTSUP (with the message set) when a map of n_entries entries does
+// not fit the 32-bit offsets of the exported layout.
+int tile_map_check_entries(size_t n_entries);
+// Largest accepted N = n_text + grid_h * grid_w: token indices, and N rounded
+// up to whole 32-key chunks, stay in 32-bit signed range in host and kernels.
+constexpr long long kMaxTokens = 0x7fffffffLL - 4096;
+// The attention kernels index entries with 32-bit signed arithmetic.
+constexpr int kMaxKernelEntries = 0x7fffffff;
+// Fills the map (entries past cap are counted, not written); returns the
+// number of entries listed, which equals tile_map_count(g).
+size_t tile_map_fill_host(const TileGeom& g, uint32_t* offsets, uint32_t* key_tiles, uint16_t* flags,
+                          size_t cap);
 
 // Lane-mask table of partly admitted chunks (tilemap_host.cpp): entries for
 // tile offsets D = (4 iy, 8 ix), |iy| <= ky, |ix| <= kx, 16 words each.  Not

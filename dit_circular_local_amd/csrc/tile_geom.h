@@ -108,6 +108,31 @@ CLEAR_HD void interval_dist(int a0, int a1, int b0, int b1, int& dmin, int& dmax
   dmax = imax(iabs(b1 - a0), iabs(a1 - b0));
 }
 
+// Number of key tiles listed for the query tile with clipped rectangle
+// [y0, y1] x [x0, x1], i.e. of key tiles some sub-tile on the grid touches.
+// Those sub-tiles form a product of row ranges and column ranges whose union
+// is the clipped rectangle, so one of them reaches both the tile's smallest
+// row distance and its smallest column distance to any key tile: a key tile is
+// listed iff the rectangle touches it.  In a key-tile row at row distance dy
+// that holds for the run of columns meeting [x0 - w, x1 + w], w being the
+// largest column distance the window admits there: isqrt(r2 - dy^2) for the
+// circle, isqrt(r2) for the square (dy^2 <= r2 in both).  O(key-tile rows).
+CLEAR_HD uint32_t listed_key_tiles(const TileGeom& g, int y0, int y1, int x0, int x1) {
+  if (g.wmax < 0) return 0;
+  const int ky_lo = imax(0, y0 - g.wmax) / g.kh, ky_hi = imin(g.gh - 1, y1 + g.wmax) / g.kh;
+  uint32_t n = 0;
+  for (int ky = ky_lo; ky <= ky_hi; ++ky) {
+    const int ky0 = ky * g.kh, ky1 = imin(g.gh, ky0 + g.kh) - 1;
+    int dymin, dymax;
+    interval_dist(y0, y1, ky0, ky1, dymin, dymax);
+    const int dy2 = dymin * dymin;
+    if (dy2 > g.r2) continue;
+    const int w = g.window == kWindowSquare ? g.wmax : isqrt_exact(g.r2 - dy2);
+    n += (uint32_t)(imin(g.gw - 1, x1 + w) / g.kw - imax(0, x0 - w) / g.kw + 1);
+  }
+  return n;
+}
+
 // Flags (bit s touched, bit 8+s full) of key tile (kty, ktx) for the query tile
 // whose top-left cell is (ty0, tx0).
 CLEAR_HD unsigned key_tile_flags(const TileGeom& g, int ty0, int tx0, int kty, int ktx) {

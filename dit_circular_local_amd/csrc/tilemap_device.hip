@@ -2,8 +2,8 @@
 //
 // Three kernels on the caller's stream, from the same closed forms as the host
 // builder (tile_geom.h), so the two agree bit for bit:
-//   1. one workgroup per query tile: number of listed key tiles, written to
-//      offsets[t];
+//   1. one thread per query tile: number of listed key tiles (the closed form
+//      listed_key_tiles), written to offsets[t];
 //   2. one workgroup: in-place exclusive scan of offsets (entry ntiles
 //      receives the total);
 //   3. one workgroup per query tile: the flags of every candidate key tile, in
@@ -23,22 +23,12 @@ constexpr int kThreads = 256;
 constexpr int kScanThreads = 1024;
 
 __global__ void __launch_bounds__(kThreads) k_tile_counts(TileGeom g, uint32_t* offsets) {
-  __shared__ uint32_t wsum[kThreads / 64];
-  const int t = blockIdx.x;
-  int y0, y1, x0, x1, kylo, kyhi, kxlo, kxhi;
+  const int nt = g.nty * g.ntx;
+  const int t = blockIdx.x * kThreads + threadIdx.x;
+  if (t >= nt) return;
+  int y0, y1, x0, x1;
   tile_rect(g, t, y0, y1, x0, x1);
-  candidate_key_tiles(g, y0, y1, x0, x1, kylo, kyhi, kxlo, kxhi);
-  const int ncx = kxhi - kxlo + 1;
-  const int ncand = kyhi >= kylo ? (kyhi - kylo + 1) * ncx : 0;
-  uint32_t n = 0;
-  for (int c = threadIdx.x; c < ncand; c += kThreads) {
-    const int ky = kylo + c / ncx, kx = kxlo + c % ncx;
-    if (key_tile_flags(g, y0, x0, ky, kx) & 0xFFu) ++n;
-  }
-  for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off);
-  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = n;
-  __syncthreads();
-  if (threadIdx.x == 0) offsets[t] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  offsets[t] = listed_key_tiles(g, y0, y1, x0, x1);
 }
 
 // In-place exclusive scan of x[0..n) with x[n] = total, by one workgroup.
@@ -78,6 +68,7 @@ __global__ void __launch_bounds__(kThreads) k_tile_fill(TileGeom g, const uint32
   const int ncx = kxhi - kxlo + 1;
   const int ncand = kyhi >= kylo ? (kyhi - kylo + 1) * ncx : 0;
   uint32_t base = offsets[t];
+  const uint32_t end = offsets[t + 1];  // entries are written only inside this tile's range
   for (int c0 = 0; c0 < ncand; c0 += kThreads) {
     const int c = c0 + (int)threadIdx.x;
     unsigned f = 0;
@@ -95,17 +86,17 @@ __global__ void __launch_bounds__(kThreads) k_tile_fill(TileGeom g, const uint32
     uint32_t woff = 0;
     for (int w = 0; w < wave; ++w) woff += wcnt[w];
     const uint32_t total = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
-    if (keep) {
-      const uint32_t e = base + woff + before;
+    const uint32_t e = base + woff + before;
+    if (keep && e < end) {
       key_tiles[e] = (uint32_t)(ky * g.nkx + kx);
       flags[e] = (uint16_t)f;
       if (desc) {
         const uint32_t tok = (uint32_t)(ky * g.kh * g.gw + kx * g.kw);
         const bool inside = ky * g.kh + g.kh <= g.gh && kx * g.kw + g.kw <= g.gw;
-        desc[4 * e + 0] = tok;
-        desc[4 * e + 1] = f | (inside ? kTileInside : 0u);
-        desc[4 * e + 2] = ((uint32_t)ky << 16) | (uint32_t)kx;
-        desc[4 * e + 3] = (uint32_t)(g.gh * g.gw) - tok;
+        desc[4 * (size_t)e + 0] = tok;
+        desc[4 * (size_t)e + 1] = f | (inside ? kTileInside : 0u);
+        desc[4 * (size_t)e + 2] = ((uint32_t)ky << 16) | (uint32_t)kx;
+        desc[4 * (size_t)e + 3] = (uint32_t)(g.gh * g.gw) - tok;
       }
     }
     base += total;
@@ -119,7 +110,7 @@ int tile_map_build_device_launch(const TileGeom& g, uint32_t* offsets, uint32_t*
                                  uint16_t* flags, uint32_t* desc, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   const int nt = g.nty * g.ntx;
-  hipLaunchKernelGGL(k_tile_counts, dim3(nt), dim3(kThreads), 0, s, g, offsets);
+  hipLaunchKernelGGL(k_tile_counts, dim3((nt + kThreads - 1) / kThreads), dim3(kThreads), 0, s, g, offsets);
   hipLaunchKernelGGL(k_scan_offsets, dim3(1), dim3(kScanThreads), 0, s, offsets, nt);
   hipLaunchKernelGGL(k_tile_fill, dim3(nt), dim3(kThreads), 0, s, g, offsets, key_tiles, flags, desc);
   const hipError_t e = hipGetLastError();

@@ -26,31 +26,30 @@ int tile_map_validate(int gh, int gw, int r2, int th, int tw, int sh, int sw, in
   return CLEAR_OK;
 }
 
-// Number of listed key tiles of query tile t.
-static uint32_t tile_entries(const TileGeom& g, int t) {
-  int y0, y1, x0, x1, kylo, kyhi, kxlo, kxhi;
-  tile_rect(g, t, y0, y1, x0, x1);
-  candidate_key_tiles(g, y0, y1, x0, x1, kylo, kyhi, kxlo, kxhi);
-  uint32_t n = 0;
-  for (int ky = kylo; ky <= kyhi; ++ky)
-    for (int kx = kxlo; kx <= kxhi; ++kx)
-      if (key_tile_flags(g, y0, x0, ky, kx) & 0xFFu) ++n;
-  return n;
-}
-
 size_t tile_map_count(const TileGeom& g) {
   size_t n = 0;
   const int nt = g.nty * g.ntx;
-  for (int t = 0; t < nt; ++t) n += tile_entries(g, t);
+  for (int t = 0; t < nt; ++t) {
+    int y0, y1, x0, x1;
+    tile_rect(g, t, y0, y1, x0, x1);
+    n += listed_key_tiles(g, y0, y1, x0, x1);
+  }
   return n;
 }
 
-void tile_map_fill_host(const TileGeom& g, uint32_t* offsets, uint32_t* key_tiles,
-                        uint16_t* flags) {
+int tile_map_check_entries(size_t n_entries) {
+  if (n_entries > 0xffffffffull)
+    return set_error(CLEAR_ENOTSUP, "the tile map holds %zu entries; its 32-bit offsets reach at most %u",
+                     n_entries, 0xffffffffu);
+  return CLEAR_OK;
+}
+
+size_t tile_map_fill_host(const TileGeom& g, uint32_t* offsets, uint32_t* key_tiles, uint16_t* flags,
+                          size_t cap) {
   const int nt = g.nty * g.ntx;
-  uint32_t e = 0;
+  size_t e = 0;
   for (int t = 0; t < nt; ++t) {
-    offsets[t] = e;
+    offsets[t] = (uint32_t)e;
     int y0, y1, x0, x1, kylo, kyhi, kxlo, kxhi;
     tile_rect(g, t, y0, y1, x0, x1);
     candidate_key_tiles(g, y0, y1, x0, x1, kylo, kyhi, kxlo, kxhi);
@@ -58,13 +57,16 @@ void tile_map_fill_host(const TileGeom& g, uint32_t* offsets, uint32_t* key_tile
       for (int kx = kxlo; kx <= kxhi; ++kx) {
         const unsigned f = key_tile_flags(g, y0, x0, ky, kx);
         if (f & 0xFFu) {
-          key_tiles[e] = (uint32_t)(ky * g.nkx + kx);
-          flags[e] = (uint16_t)f;
+          if (e < cap) {
+            key_tiles[e] = (uint32_t)(ky * g.nkx + kx);
+            flags[e] = (uint16_t)f;
+          }
           ++e;
         }
       }
   }
-  offsets[nt] = e;
+  offsets[nt] = (uint32_t)e;
+  return e;
 }
 
 }  // namespace clear
@@ -141,11 +143,16 @@ extern "C" int clear_tile_map_build_ex(int window, int grid_h, int grid_w, int r
   if (!n_entries) return set_error(CLEAR_EINVAL, "n_entries must not be NULL");
   TileGeom g = make_geom(grid_h, grid_w, r2_max, tile_h, tile_w, sub_h, sub_w, key_h, key_w, window);
   *n_entries = tile_map_count(g);
+  rc = tile_map_check_entries(*n_entries);
+  if (rc) return rc;
   if (*n_entries > cap)
     return set_error(CLEAR_ENOMEM, "tile map needs %zu entries (capacity %zu)", *n_entries, cap);
   if (!offsets || (*n_entries && (!key_tiles || !flags)))
     return set_error(CLEAR_EINVAL, "tile map output pointers must not be NULL");
-  tile_map_fill_host(g, offsets, key_tiles, flags);
+  const size_t filled = tile_map_fill_host(g, offsets, key_tiles, flags, *n_entries);
+  if (filled != *n_entries)
+    return set_error(CLEAR_EINVAL, "internal: tile map count %zu differs from the %zu entries listed", *n_entries,
+                     filled);
   return CLEAR_OK;
 }
 

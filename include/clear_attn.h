@@ -100,7 +100,7 @@ typedef struct clear_opts {
  *             16-byte aligned.  Caller-owned, read only.
  *   out     : device, [B, H, N, d] contiguous bfloat16; caller-owned; must not
  *             overlap q, k or v.  Every element is written.
- *   B, H    : >= 1.  d: 64 or 128.  n_text >= 0.
+ *   B, H    : >= 1.  d: 64 or 128.  n_text >= 0; N at most 2^31 - 4097.
  *   grid_h, grid_w : 1 .. CLEAR_MAX_GRID.  radius >= 0.
  *   n_text == 0 with an empty window cannot happen here (radius >= 0 admits
  *   the query itself).
@@ -109,6 +109,10 @@ typedef struct clear_opts {
  * rounded to bf16.
  * The library builds (on the stream, once per (grid_h, grid_w, r2)) and caches
  * the tile map, and owns the text-row workspace; see clear_release_cache.
+ * Returns CLEAR_ENOTSUP, launching nothing, when that tile map would list more
+ * than 2^31 - 1 key tiles (the kernels' 32-bit signed entry index): only huge
+ * grids at large radii: from r = 197 on an 8192 x 8192 grid.  Every entry
+ * point that attends (forward, strips, backward) shares this limit.
  */
 int clear_attn_fwd(const void* q, const void* k, const void* v, void* out,
                    int B, int H, int d, int n_text, int grid_h, int grid_w,
@@ -240,6 +244,8 @@ int clear_tile_map_size(int grid_h, int grid_w, int r2_max, int tile_h, int tile
  *                            tile is listed iff some bit 0..7 is set.
  * cap is the capacity of key_tiles / flags.  If it is too small, returns
  * CLEAR_ENOMEM with *n_entries set and nothing written (cap 0 queries the size).
+ * A map of more than 2^32 - 1 entries does not fit the 32-bit offsets: then
+ * CLEAR_ENOTSUP, with *n_entries set and nothing written.
  */
 int clear_tile_map_build(int grid_h, int grid_w, int r2_max, int tile_h, int tile_w,
                          int sub_h, int sub_w, int key_h, int key_w, uint32_t* offsets,
@@ -250,7 +256,8 @@ int clear_tile_map_build(int grid_h, int grid_w, int r2_max, int tile_h, int til
  * clear_tile_map_build_device -- the same tile map, built by kernels on `stream`
  * into device buffers (same layout and contents, bit for bit, as the host
  * builder).  The size is computed on the host first; if cap is too small it
- * returns CLEAR_ENOMEM with *n_entries (a host pointer) set and launches nothing.
+ * returns CLEAR_ENOMEM with *n_entries (a host pointer) set and launches nothing
+ * (CLEAR_ENOTSUP likewise above 2^32 - 1 entries).
  */
 int clear_tile_map_build_device(int grid_h, int grid_w, int r2_max, int tile_h,
                                 int tile_w, int sub_h, int sub_w, int key_h, int key_w,

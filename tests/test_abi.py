@@ -57,6 +57,7 @@ def _fwd_ex(dtype=0, r2=4, lse=None, splits=0, q=Q, k=K, v=V, o=O, **kw):
     (dict(gh=0), "grid sides"), (dict(gw=8193), "grid sides"),
     (dict(q=0), "NULL"), (dict(o=0), "NULL"), (dict(q=Q + 8), "aligned"),
     (dict(o=Q + 4096), "overlap"), (dict(o=V - 16), "overlap"),
+    (dict(n_text=2 ** 31 - 4096 - 16), "sequence too long"),
 ])
 def test_fwd_rejects_bad_arguments(kw, frag):
     assert _fwd(**kw) == ca.CLEAR_EINVAL
@@ -118,6 +119,7 @@ def _bwd(dtype=0, r2=4, lse_out=None, splits=0, window=0, q=Q, k=K, v=V, o=O, do
     (dict(dq=DO - 16), "overlap"), (dict(lse=LSE + 2), "lse must be"), (dict(dk=DK + 8), "aligned"),
     (dict(lse_out=0x1000), "lse_out"), (dict(splits=65), "text_splits"), (dict(window=3), "window"),
     (dict(dtype=7), "dtype"), (dict(r2=-3), "r2_max"), (dict(n_text=0, r2=-1), "empty"),
+    (dict(n_text=2 ** 31 - 4096 - 16), "sequence too long"),
 ])
 def test_bwd_rejects_bad_arguments(kw, frag):
     assert _bwd(**kw) == ca.CLEAR_EINVAL

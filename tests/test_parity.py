@@ -296,3 +296,47 @@ def test_degenerate_grids(n_text, gh, gw, r2):
     """One image token, one row, one column (with and without text), fp32,
     every output element and the LSE against the oracle."""
     _check_full("fp32", 1, 2, n_text, gh, gw, 64, r2)
+
+
+def test_full_grid_heads_beyond_4_gb():
+    """The largest grid, 8192 x 8192 with 2 text tokens (N = 67,108,866), bf16,
+    d 128: one head of K is 17.2 GB, so key offsets within a head pass 2^31,
+    2^32 and 2^33 bytes.
+    * r = 197 would list more key tiles than the kernels index (2^31 - 1): the
+      call fails with CLEAR_ENOTSUP before launching anything.
+    * r = 2: image rows at the corners, the middle and on both sides of the
+      2^31 / 2^32 / 2^33-byte token offsets against the oracle on the window box
+      around each cell (an exact sub-problem, see tests/window_box.py).
+    * Text rows: their queries are zero, so every key weighs the same; with V
+      the indicator of 128 consecutive key ranges times 128, output column c is
+      128 x (range c's share of the keys), about 1.  A key range lost or counted
+      twice by the split text rows moves its column by its share."""
+    from window_box import box_reference
+
+    G, n_text, d = ca.MAX_GRID, 2, 128
+    N = n_text + G * G
+    gen = torch.Generator(device="cuda").manual_seed(71)
+    q, k, v = (torch.randn(1, 1, N, d, device="cuda", dtype=torch.bfloat16, generator=gen) for _ in range(3))
+    q[0, 0, :n_text] = 0
+    with pytest.raises(ca.ClearError) as err:
+        ca.fwd(q, k, v, n_text, G, G, radius=197)
+    assert err.value.code == ca.CLEAR_ENOTSUP
+
+    out = _run(q, k, v, n_text, G, G, 4)
+    row_bytes = d * 2
+    toks = [N - 1] + [b // row_bytes + s for b in (2 ** 31, 2 ** 32, 2 ** 33) for s in (-1, 0, 1)]
+    cells = [(0, 0), (0, G - 1), (G - 1, 0), (G // 2, G // 2)] + [divmod(t - n_text, G) for t in toks]
+    rows, ref = box_reference(q[0, 0], k[0, 0], v[0, 0], n_text, G, G, 4, cells)
+    err_img = np.abs(_np(out[0, 0, rows]) - ref).max()
+    assert err_img <= TOL["bf16"], f"image rows: max-abs {err_img:.3e}"
+
+    del out
+    blk = torch.arange(N, device="cuda") * 128 // N
+    v.zero_()
+    v[0, 0, torch.arange(N, device="cuda"), blk] = 128.0
+    out = _run(q, k, v, n_text, G, G, 4)
+    want = 128.0 * torch.bincount(blk, minlength=128).double().cpu().numpy() / N
+    err_txt = np.abs(_np(out[0, 0, :n_text]) - want[None, :]).max()
+    assert err_txt <= TOL["bf16"], f"text rows: max-abs {err_txt:.3e}"
+    del q, k, v, out, blk
+    torch.cuda.empty_cache()

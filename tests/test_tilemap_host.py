@@ -1,5 +1,7 @@
 """The library's host tile-map builder against the oracle's brute force, bit for bit."""
 
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -82,3 +84,39 @@ def test_unknown_window_is_rejected():
         ca.tile_map_build(8, 8, 4, window="hexagon")
     rc = ca.lib().clear_tile_map_size_ex(7, 8, 8, 4, 16, 8, 4, 8, 4, 8, None)
     assert rc == ca.CLEAR_EINVAL
+
+
+def test_entry_count_matches_the_listing_on_random_geometries():
+    """The size query counts each key-tile row's run of listed columns in closed
+    form; the builder lists key tiles one by one.  Both must equal the oracle's
+    brute-force count over random grids, radii, tilings and both windows."""
+    rng = np.random.default_rng(7)
+    for _ in range(60):
+        sh, sw = int(rng.integers(1, 5)), int(rng.integers(1, 5))
+        nsy, nsx = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        th, tw = sh * nsy, sw * nsx
+        kh, kw = int(rng.integers(1, 9)), int(rng.integers(1, 9))
+        gh, gw = int(rng.integers(1, 40)), int(rng.integers(1, 40))
+        r2 = int(rng.integers(-1, (gh - 1) ** 2 + (gw - 1) ** 2 + 3))
+        window = ("circle", "square")[int(rng.integers(0, 2))]
+        args = (gh, gw, r2, th, tw, sh, sw, kh, kw)
+        n = ca.tile_map_size(*args, window=window)
+        ref = tile_map_bruteforce(*args, window=window)
+        assert n == len(ref["key_tiles"]), (args, window)
+        _same(ca.tile_map_build(*args, window=window), ref)
+
+
+def test_maps_beyond_32_bit_offsets_are_rejected():
+    """An 8192 x 8192 grid at r = 400 lists about 8.7e9 key tiles: the size
+    query returns the count (in closed form, without listing them) and the
+    builder, whose offsets are 32-bit, refuses it with nothing written."""
+    g, r = ca.MAX_GRID, 400
+    n = ca.tile_map_size(g, g, r * r)
+    assert n > 2 ** 32 - 1
+    got = ctypes.c_size_t()
+    off = np.zeros(4, np.uint32)
+    rc = ca.lib().clear_tile_map_build_ex(0, g, g, r * r, ca.TILE_H, ca.TILE_W, ca.SUB_H, ca.SUB_W, ca.KEY_H,
+                                          ca.KEY_W, off.ctypes.data, None, None, 0, ctypes.byref(got))
+    assert rc == ca.CLEAR_ENOTSUP and got.value == n
+    assert not off.any()
+    assert "32-bit" in ca.lib().clear_last_error().decode()

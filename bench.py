@@ -82,8 +82,9 @@ def computed_pairs(ca, n_text: int, gh: int, gw: int, r2: int, window: str = "ci
     return (dense + touched + text_rows) * per_chunk
 
 
-# sources the forward attention kernel is compiled from (its traffic figures
-# hold only while these are unchanged)
+# sources the forward attention kernel is compiled from; with the device
+# code-generation flags they key its traffic figures, which hold only while
+# both are unchanged
 FWD_KERNEL_SOURCES = ("dit_circular_local_amd/csrc/attn_fwd.hip", "dit_circular_local_amd/csrc/attn_common.h",
                       "dit_circular_local_amd/csrc/clear_internal.h", "dit_circular_local_amd/csrc/tile_geom.h",
                       "include/clear_attn.h")
@@ -104,12 +105,15 @@ def kernel_source_hash() -> str:
     for name in FWD_KERNEL_SOURCES:
         with open(os.path.join(ROOT, name), encoding="utf-8") as f:
             h.update(name.encode() + _code_only(f.read()).encode())
+    from dit_circular_local_amd.build import DEVICE_FLAGS
+
+    h.update(" ".join(DEVICE_FLAGS).encode())
     return h.hexdigest()[:16]
 
 
 def load_traffic(workload: str, radius: int):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources (else None)."""
+    taken on the current kernel sources and device flags (else None)."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None

@@ -16,13 +16,22 @@ SOURCES = ["clear_attn.cpp", "tilemap_host.cpp", "tilemap_device.hip", "attn_fwd
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
+# Code-generation flags of the device code (part of what the kernels are).
+DEVICE_FLAGS = [
+    # packed fp32 VALU forms are kept out of the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # branches on wavefront-uniform values stay plain scalar branches: the CFG
+    # structurizer would otherwise join them through flow blocks whose
+    # conditions it carries as 64-bit lane masks (scalar work on every chunk)
+    "-Xarch_device", "-mllvm=-structurizecfg-skip-uniform-regions=true",
+]
+
 
 def build_command(out: str = LIB):
     return [
         HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-Wall", "-Wno-unused-function",
-        # packed fp32 VALU forms are kept out of the device code
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        *DEVICE_FLAGS,
         "-I", INCLUDE, "-I", CSRC,
         *[os.path.join(CSRC, s) for s in SOURCES],
         "-o", out,

@@ -142,11 +142,23 @@ __device__ __forceinline__ ChunkInfo tile_chunk_info(const ChunkMeta& m, const K
                    (m.flag & kTileInside) != 0, kChunk, kty, ktx, kty * kKeyH, ktx * kKeyW};
 }
 
+// Barrier of the chunk walk.  Direct-to-LDS copies are vector-memory loads
+// that write LDS: the compiler orders them only against the same wavefront's
+// later LDS reads, and the barrier's fence need not wait for them, so a
+// wavefront could pass the barrier with its last copy still landing while the
+// others start reading that stage.  Each wavefront therefore first waits for
+// all of its own copies (vmcnt(0)); after the barrier every wavefront's copies
+// of the stage are complete.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
 // The chunk walk of the attention kernels.  Two LDS stages: after the
 // barrier of iteration j, chunk j is in its stage (the copies were issued in
-// iteration j - 1 and the barrier waits for every wavefront's copies), and
-// every wavefront is done with chunk j - 1, so the copies of chunk j + 1 go to
-// the other stage while chunk j is computed.  The descriptor of chunk j + 2 is
+// iteration j - 1, and stage_barrier has every wavefront wait for its own),
+// and every wavefront is done with chunk j - 1, so the copies of chunk j + 1
+// go to the other stage while chunk j is computed.  The descriptor of chunk j + 2 is
 // fetched in iteration j, so its scalar load is complete when needed.
 //   stage(st, meta, dense) issues the copies of a chunk into stage st;
 //   compute(info, st) computes the chunk held in st.
@@ -167,7 +179,7 @@ __device__ __forceinline__ void walk_chunks(const KeySource& ks, int n, int wave
   ChunkMeta m_nxt = chunk_meta(ks, n > 1 ? 1 : 0);
   stage(st_cur, m_cur, 0 < ks.n_dense);
   auto dense_step = [&](int jj, ChunkMeta& mc, const ChunkMeta& mn, const char* cur, char* nxt) {
-    __syncthreads();
+    stage_barrier();
     if (jj + 1 < n) stage(nxt, mn, jj + 1 < ks.n_dense);
     const ChunkInfo c = dense_chunk_info(mc, ks);
     mc = chunk_meta(ks, jj + 2 < n ? jj + 2 : n - 1);
@@ -190,7 +202,7 @@ __device__ __forceinline__ void walk_chunks(const KeySource& ks, int n, int wave
     st_nxt = t;
   }
   auto tile_step = [&](int jj, ChunkMeta& mc, const ChunkMeta& mn, const char* cur, char* nxt) {
-    __syncthreads();
+    stage_barrier();
     if (jj + 1 < n) stage(nxt, mn, false);
     const ChunkInfo c = tile_chunk_info(mc, ks, wave);
     mc = tile_chunk_meta(ks, jj + 2 < n ? jj + 2 : n - 1);

@@ -37,6 +37,10 @@ struct DevState {
   std::map<std::tuple<int, int, int, int>, TileMapDev> maps;  // (gh, gw, r2, window)
   void* ws = nullptr;
   size_t ws_bytes = 0;
+  // the last call that used the workspace: its stream and an event recorded
+  // after its kernels, which a call on another stream waits for
+  hipEvent_t ws_done = nullptr;
+  hipStream_t ws_stream = nullptr;
 };
 
 std::mutex g_mu;
@@ -132,8 +136,12 @@ int choose_text_splits(int B, int H, int n_text, int N, int ntiles, size_t img_c
   return s;
 }
 
-// Grow the device's library workspace to at least `need` bytes.  Caller holds g_mu.
-int workspace(DevState& ds, size_t need, void** out) {
+// The device's library workspace, grown to at least `need` bytes, for kernels
+// about to be enqueued on stream s.  If the previous user ran on another
+// stream, s first waits (on the device) for that user's kernels, so calls on
+// different streams take turns with the buffer; workspace_done records the
+// end of this call's use.  Caller holds g_mu.
+int workspace(DevState& ds, size_t need, hipStream_t s, void** out) {
   if (need > ds.ws_bytes) {
     hipError_t e;
     // the old workspace may still be read by queued kernels
@@ -147,7 +155,20 @@ int workspace(DevState& ds, size_t need, void** out) {
       return set_error(CLEAR_ENOMEM, "workspace (%zu bytes): %s", need, hipGetErrorString(e));
     ds.ws_bytes = need;
   }
+  if (ds.ws_done && ds.ws_stream != s) {
+    hipError_t e = hipStreamWaitEvent(s, ds.ws_done, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (workspace)");
+  }
   *out = ds.ws;
+  return CLEAR_OK;
+}
+
+int workspace_done(DevState& ds, hipStream_t s) {
+  hipError_t e;
+  if (!ds.ws_done && (e = hipEventCreateWithFlags(&ds.ws_done, hipEventDisableTiming)) != hipSuccess)
+    return hip_fail(e, "hipEventCreateWithFlags (workspace)");
+  if ((e = hipEventRecord(ds.ws_done, s)) != hipSuccess) return hip_fail(e, "hipEventRecord (workspace)");
+  ds.ws_stream = s;
   return CLEAR_OK;
 }
 
@@ -272,12 +293,13 @@ int run_forward(const void* q, const void* k, const void* v, void* out, int B, i
     const size_t o_bytes = align_up((size_t)splits * B * H * n_text * d * 4, 256);
     const size_t need = o_bytes + (size_t)splits * B * H * n_text * 2 * 4;
     void* ws = nullptr;
-    if ((rc = workspace(ds, need, &ws)) != CLEAR_OK) return rc;
+    if ((rc = workspace(ds, need, s, &ws)) != CLEAR_OK) return rc;
     a.ws_o = (float*)ws;
     a.ws_ml = (float*)((char*)ws + o_bytes);
   }
   rc = attn_launch(a, stream);
   if (rc) return rc;
+  if (a.ws_o && !strip && (rc = workspace_done(ds, s)) != CLEAR_OK) return rc;
   if (debug_sync_enabled()) {
     if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "CLEAR_DEBUG sync");
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "CLEAR_DEBUG check");
@@ -348,7 +370,7 @@ int run_backward(const void* q, const void* k, const void* v, const void* out, c
   const size_t stats_bytes = align_up((size_t)B * H * (size_t)N * 8, 256);
   const size_t part_bytes = n_text > 0 ? align_up((size_t)splits * B * H * n_text * d * 4, 256) : 0;
   void* ws = nullptr;
-  if ((rc = workspace(ds, stats_bytes + 3 * part_bytes, &ws)) != CLEAR_OK) return rc;
+  if ((rc = workspace(ds, stats_bytes + 3 * part_bytes, s, &ws)) != CLEAR_OK) return rc;
 
   BwdLaunch a;
   memset(&a, 0, sizeof a);
@@ -366,6 +388,7 @@ int run_backward(const void* q, const void* k, const void* v, const void* out, c
   a.dtype = o.dtype; a.text_splits = splits; a.window = o.window;
   rc = attn_bwd_launch(a, stream);
   if (rc) return rc;
+  if ((rc = workspace_done(ds, s)) != CLEAR_OK) return rc;
   if (debug_sync_enabled()) {
     if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "CLEAR_DEBUG sync");
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "CLEAR_DEBUG check");
@@ -494,6 +517,9 @@ extern "C" void clear_release_cache(void) {
     if (kv.second.ws) (void)hipFree(kv.second.ws);
     kv.second.ws = nullptr;
     kv.second.ws_bytes = 0;
+    if (kv.second.ws_done) (void)hipEventDestroy(kv.second.ws_done);
+    kv.second.ws_done = nullptr;
+    kv.second.ws_stream = nullptr;
   }
   (void)hipSetDevice(cur);
 }

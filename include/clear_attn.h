@@ -39,8 +39,10 @@
  *     threads; the library's caches are guarded by a mutex.  Calls that use
  *     the library's workspace (the text-row partials of clear_attn_fwd* and
  *     the statistics and partials of clear_attn_bwd) share one buffer per
- *     device: calls on one stream are ordered and safe; calls running
- *     concurrently on different streams of one device race on it.
+ *     device.  Calls on one stream are ordered by the stream; a call on
+ *     another stream than the previous user of the buffer first makes its
+ *     stream wait (on the device, by an event) for that user's kernels, so
+ *     such calls take turns with the buffer instead of overlapping.
  */
 #ifndef CLEAR_ATTN_H
 #define CLEAR_ATTN_H

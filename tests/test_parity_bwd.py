@@ -202,3 +202,36 @@ def test_degenerate_grids(n_text, gh, gw, r2):
     """One image token, one row, one column (with and without text), fp32,
     every gradient element against the oracle."""
     _check("fp32", 1, 2, n_text, gh, gw, 64, r2)
+
+
+def test_calls_on_two_streams_take_turns_with_the_workspace():
+    """Forwards with their text rows split in four (partials in the library's
+    workspace) and backwards (statistics and partials there too) alternate
+    between two streams with no host synchronisation in between: every output
+    equals, bit for bit, the same call made alone on one stream."""
+    n_text, g, d = 512, 64, 128
+    N = n_text + g * g
+    cases = []
+    for seed in (1, 2):
+        q, k, v = make_qkv(1, 4, n_text, g, g, d, "bf16", seed, device="cuda")
+        do = make_dout(1, 4, N, d, "bf16", seed, device="cuda")
+        cases.append((q, k, v, do))
+    refs = []
+    for q, k, v, do in cases:
+        out, lse = ca.fwd(q, k, v, n_text, g, g, radius=16, text_splits=4, return_lse=True)
+        grads = ca.bwd(q, k, v, out, do, lse, n_text, g, g, radius=16, text_splits=4)
+        torch.cuda.synchronize()
+        refs.append((out, lse, grads))
+    streams = (torch.cuda.Stream(), torch.cuda.Stream())
+    results = []
+    for _ in range(3):
+        for i, (q, k, v, do) in enumerate(cases):
+            with torch.cuda.stream(streams[i]):
+                out, lse = ca.fwd(q, k, v, n_text, g, g, radius=16, text_splits=4, return_lse=True)
+                grads = ca.bwd(q, k, v, refs[i][0], do, refs[i][1], n_text, g, g, radius=16, text_splits=4)
+                results.append((i, out, lse, grads))
+    torch.cuda.synchronize()
+    for i, out, lse, grads in results:
+        assert torch.equal(out, refs[i][0]) and torch.equal(lse, refs[i][1]), f"forward, case {i}"
+        for name, a, b in zip(("dq", "dk", "dv"), grads, refs[i][2]):
+            assert torch.equal(a, b), f"{name}, case {i}"

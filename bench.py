@@ -82,12 +82,12 @@ def computed_pairs(ca, n_text: int, gh: int, gw: int, r2: int, window: str = "ci
     return (dense + touched + text_rows) * per_chunk
 
 
-# sources the forward attention kernel is compiled from; with the device
-# code-generation flags they key its traffic figures, which hold only while
-# both are unchanged
+# sources the forward attention kernel is compiled and launched from (launch
+# configuration included); with the device code-generation flags they key its
+# traffic figures, which hold only while both are unchanged
 FWD_KERNEL_SOURCES = ("dit_circular_local_amd/csrc/attn_fwd.hip", "dit_circular_local_amd/csrc/attn_common.h",
                       "dit_circular_local_amd/csrc/clear_internal.h", "dit_circular_local_amd/csrc/tile_geom.h",
-                      "include/clear_attn.h")
+                      "include/clear_attn.h", "dit_circular_local_amd/csrc/clear_attn.cpp")
 
 
 def _code_only(text: str) -> str:

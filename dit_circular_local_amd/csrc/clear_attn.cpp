@@ -41,10 +41,27 @@ struct DevState {
   // after its kernels, which a call on another stream waits for
   hipEvent_t ws_done = nullptr;
   hipStream_t ws_stream = nullptr;
+  // compute units of the device (a partitioned MI355X exposes fewer than 256)
+  int n_cu = 0;
 };
+
 
 std::mutex g_mu;
 std::map<int, DevState> g_dev;
+
+// The device's state, with its compute-unit count read on first use.  Caller
+// holds g_mu.
+int dev_state(int dev, DevState** out) {
+  DevState& ds = g_dev[dev];
+  if (ds.n_cu <= 0) {
+    int n = 0;
+    hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return set_error(CLEAR_EHIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+    ds.n_cu = n > 0 ? n : 256;
+  }
+  *out = &ds;
+  return CLEAR_OK;
+}
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -120,7 +137,7 @@ int get_tile_map(DevState& ds, int gh, int gw, int r2, int window, hipStream_t s
 // one workgroup slot each across the chip: on the 512x512 + 512 FLUX shape
 // (24 heads) that is 8 splits, measured 1.5-3 % faster than the 2 (r = 32) and
 // 5 (r = 8) of the critical-path rule alone, and neutral on 256x256 + 512.
-int choose_text_splits(int B, int H, int n_text, int N, int ntiles, size_t img_chunks,
+int choose_text_splits(int B, int H, int n_text, int N, int ntiles, size_t img_chunks, int n_cu,
                        double waves_per_simd = 3.0, bool fill_slots = false) {
   // img_chunks: listed key tiles (32 keys each) over all query tiles
   if (n_text == 0) return 1;
@@ -130,11 +147,11 @@ int choose_text_splits(int B, int H, int n_text, int N, int ntiles, size_t img_c
   // wavefront-chunks of work (each = 32 queries x 32 keys)
   const double w_img = (double)B * H * (4.0 * ntiles * nt_ch + 3.0 * (double)img_chunks);
   const double w_text = (double)B * H * text_blocks * 4.0 * nall;
-  const double slots = 256.0 * 4.0 * waves_per_simd;  // CUs x SIMDs x resident waves
+  const double slots = (double)n_cu * 4.0 * waves_per_simd;  // CUs x SIMDs x resident waves
   const double t_ideal = (w_img + w_text) / slots;
   int s = (int)(2.0 * nall / (t_ideal > 1.0 ? t_ideal : 1.0)) + 1;
   if (fill_slots) {
-    const double wg_slots = 256.0 * waves_per_simd;  // workgroups of 4 wavefronts resident on the chip
+    const double wg_slots = (double)n_cu * waves_per_simd;  // workgroups of 4 wavefronts resident on the device
     const int s_fill = (int)(wg_slots / ((double)B * H * text_blocks));
     if (s_fill > s) s = s_fill;
   }
@@ -273,9 +290,12 @@ int run_forward(const void* q, const void* k, const void* v, void* out, int B, i
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
 
   std::lock_guard<std::mutex> lock(g_mu);
-  DevState& ds = g_dev[dev];
+  DevState* dsp = nullptr;
+  int rc = dev_state(dev, &dsp);
+  if (rc) return rc;
+  DevState& ds = *dsp;
   TileMapDev* tm = nullptr;
-  int rc = get_tile_map(ds, grid_h, grid_w, o.r2_max, o.window, s, &tm);
+  rc = get_tile_map(ds, grid_h, grid_w, o.r2_max, o.window, s, &tm);
   if (rc) return rc;
   if ((e = hipStreamWaitEvent(s, tm->ready, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
 
@@ -283,8 +303,8 @@ int run_forward(const void* q, const void* k, const void* v, void* out, int B, i
                          CLEAR_KEY_H, CLEAR_KEY_W, o.window);
   int splits = strip ? 1
                      : o.text_splits ? o.text_splits
-                                     : choose_text_splits(B, H, n_text, (int)N, g.nty * g.ntx, tm->n_entries, 3.0,
-                                                          true);
+                                     : choose_text_splits(B, H, n_text, (int)N, g.nty * g.ntx, tm->n_entries,
+                                                          ds.n_cu, 3.0, true);
   AttnLaunch a;
   memset(&a, 0, sizeof a);
   a.q = q; a.k = k; a.v = v; a.out = out; a.lse = o.lse_out;
@@ -367,16 +387,20 @@ int run_backward(const void* q, const void* k, const void* v, const void* out, c
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
 
   std::lock_guard<std::mutex> lock(g_mu);
-  DevState& ds = g_dev[dev];
+  DevState* dsp = nullptr;
+  int rc = dev_state(dev, &dsp);
+  if (rc) return rc;
+  DevState& ds = *dsp;
   TileMapDev* tm = nullptr;
-  int rc = get_tile_map(ds, grid_h, grid_w, o.r2_max, o.window, s, &tm);
+  rc = get_tile_map(ds, grid_h, grid_w, o.r2_max, o.window, s, &tm);
   if (rc) return rc;
   if ((e = hipStreamWaitEvent(s, tm->ready, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
 
   TileGeom g = make_geom(grid_h, grid_w, o.r2_max, CLEAR_TILE_H, CLEAR_TILE_W, CLEAR_SUB_H, CLEAR_SUB_W,
                          CLEAR_KEY_H, CLEAR_KEY_W, o.window);
   const int splits = o.text_splits ? o.text_splits
-                                   : choose_text_splits(B, H, n_text, (int)N, g.nty * g.ntx, tm->n_entries, 2.0);
+                                   : choose_text_splits(B, H, n_text, (int)N, g.nty * g.ntx, tm->n_entries,
+                                                        ds.n_cu, 2.0);
   const size_t stats_bytes = align_up((size_t)B * H * (size_t)N * 8, 256);
   const size_t part_bytes = n_text > 0 ? align_up((size_t)splits * B * H * n_text * d * 4, 256) : 0;
   void* ws = nullptr;

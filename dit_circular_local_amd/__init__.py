@@ -19,7 +19,7 @@ import numpy as np
 
 __all__ = [
     "ClearError", "fwd", "bwd", "fwd_strip", "text_merge", "strip_rows", "tile_map_size", "tile_map_build", "tile_map_build_device",
-    "release_cache", "last_error", "version", "lib", "EXPORTS",
+    "tile_map_descriptors", "release_cache", "last_error", "version", "lib", "EXPORTS",
     "CLEAR_OK", "CLEAR_EINVAL", "CLEAR_ENOMEM", "CLEAR_EHIP", "CLEAR_ENOTSUP",
     "CLEAR_BF16", "CLEAR_FP32", "CLEAR_MERGE_EXACT", "CLEAR_MERGE_PATCH_AVERAGE", "CLEAR_WINDOW_CIRCLE", "CLEAR_WINDOW_SQUARE", "WINDOWS", "TILE_H", "TILE_W", "SUB_H", "SUB_W", "KEY_H", "KEY_W", "CHUNK",
     "MAX_GRID",
@@ -40,7 +40,7 @@ EXPORTS = (
     "clear_attn_fwd", "clear_attn_fwd_ex", "clear_tile_map_size", "clear_tile_map_build",
     "clear_tile_map_build_device", "clear_tile_map_size_ex", "clear_tile_map_build_ex",
     "clear_tile_map_build_device_ex", "clear_attn_fwd_strip", "clear_text_merge", "clear_attn_bwd",
-    "clear_last_error",
+    "clear_tile_map_descriptors", "clear_last_error",
     "clear_release_cache", "clear_version",
 )
 
@@ -85,6 +85,8 @@ def lib():
     L.clear_tile_map_build_ex.restype = i
     L.clear_tile_map_build_device_ex.argtypes = [i] + L.clear_tile_map_build_device.argtypes
     L.clear_tile_map_build_device_ex.restype = i
+    L.clear_tile_map_descriptors.argtypes = [i, i, i, i, p, p, p, p, sz, szp, p]
+    L.clear_tile_map_descriptors.restype = i
     L.clear_attn_fwd_strip.argtypes = [p, p, p, p, i, i, i, i, i, i, ctypes.POINTER(_Opts), i, i, i, p, p, p]
     L.clear_attn_fwd_strip.restype = i
     L.clear_text_merge.argtypes = [p, p, i, i, p, p, i, i, i, i, i, i, i, p]
@@ -129,6 +131,22 @@ def _window_code(window: str) -> int:
     return WINDOWS[window]
 
 
+def _expect(t, name: str, device, dtype, shape) -> None:
+    """Raise unless ``t`` is a contiguous GPU tensor on ``device`` with the given
+    dtype and shape.  Every buffer the library writes or reads goes through this
+    before any launch: the C ABI sees only addresses and cannot tell a host
+    pointer, a tensor on another device or a too-small element type from a good
+    one."""
+    if not getattr(t, "is_cuda", False) or t.device != device:
+        raise ValueError(f"{name} must be a GPU tensor on {device} (got {getattr(t, 'device', type(t))})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
 def fwd(q, k, v, n_text: int, grid_h: int, grid_w: int, radius: Optional[int] = None,
         r2: Optional[int] = None, out=None, return_lse: bool = False, text_splits: int = 0,
         use_ex: Optional[bool] = None, window: str = "circle"):
@@ -141,20 +159,7 @@ def fwd(q, k, v, n_text: int, grid_h: int, grid_w: int, radius: Optional[int] = 
     """
     import torch
 
-    if q.dtype != k.dtype or q.dtype != v.dtype:
-        raise TypeError("q, k, v must share a dtype")
-    if q.dtype == torch.bfloat16:
-        dtype = CLEAR_BF16
-    elif q.dtype == torch.float32:
-        dtype = CLEAR_FP32
-    else:
-        raise TypeError(f"unsupported dtype {q.dtype}")
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must all be [B, H, N, d]")
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
-        raise ValueError("q, k, v must be GPU tensors")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous")
+    dtype = _check_qkv(q, k, v)
     B, H, N, d = q.shape
     if N != n_text + grid_h * grid_w:
         raise ValueError(f"N = {N} != n_text + grid_h * grid_w = {n_text + grid_h * grid_w}")
@@ -162,8 +167,8 @@ def fwd(q, k, v, n_text: int, grid_h: int, grid_w: int, radius: Optional[int] = 
         raise ValueError("give exactly one of radius and r2")
     if out is None:
         out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    else:
+        _expect(out, "out", q.device, q.dtype, q.shape)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
     stream = _stream_of(q)
     L = lib()
@@ -203,6 +208,8 @@ def _check_qkv(q, k, v):
         raise ValueError("q, k, v must all be [B, H, N, d]")
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be GPU tensors")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one device")
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous")
     return dtype
@@ -220,12 +227,9 @@ def bwd(q, k, v, out, dout, lse, n_text: int, grid_h: int, grid_w: int, radius: 
     B, H, N, d = q.shape
     if N != n_text + grid_h * grid_w:
         raise ValueError(f"N = {N} != n_text + grid_h * grid_w = {n_text + grid_h * grid_w}")
-    for name, t in (("out", out), ("dout", dout)):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"{name} must be a contiguous GPU tensor shaped and typed like q")
-    if (tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous()
-            or not lse.is_cuda):
-        raise ValueError("lse must be a contiguous float32 GPU tensor [B, H, N]")
+    _expect(out, "out", q.device, q.dtype, q.shape)
+    _expect(dout, "dout", q.device, q.dtype, q.shape)
+    _expect(lse, "lse", q.device, torch.float32, (B, H, N))
     if (radius is None) == (r2 is None):
         raise ValueError("give exactly one of radius and r2")
     if r2 is None:
@@ -234,9 +238,10 @@ def bwd(q, k, v, out, dout, lse, n_text: int, grid_h: int, grid_w: int, radius: 
         r2 = min(int(radius) * int(radius), 2 ** 31 - 1)
     if grads is None:
         grads = tuple(torch.empty_like(q) for _ in range(3))
-    for t in grads:
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError("dq, dk, dv must be contiguous tensors shaped and typed like q")
+    if len(grads) != 3:
+        raise ValueError("grads must be (dq, dk, dv)")
+    for name, t in zip(("dq", "dk", "dv"), grads):
+        _expect(t, name, q.device, q.dtype, q.shape)
     dq, dk, dv = grads
     opts = _Opts(dtype, int(r2), None, int(text_splits), _window_code(window))
     _check(lib().clear_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
@@ -268,11 +273,12 @@ def fwd_strip(q, k, v, n_text: int, grid_h: int, grid_w: int, row_begin: int, ro
         raise ValueError("give exactly one of radius and r2")
     if r2 is None:
         r2 = min(int(radius) * int(radius), 2 ** 31 - 1)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor shaped and typed like q")
-    for t, shape in ((part_o, (B * H, n_text, d)), (part_ml, (B * H, n_text, 2))):
-        if n_text and (tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda):
-            raise ValueError(f"partial buffers must be contiguous GPU tensors of shape {shape}")
+    import torch
+
+    _expect(out, "out", q.device, q.dtype, q.shape)
+    if n_text:
+        _expect(part_o, "part_o", q.device, torch.float32, (B * H, n_text, d))
+        _expect(part_ml, "part_ml", q.device, torch.float32, (B * H, n_text, 2))
     opts = _Opts(dtype, int(r2), None, 0, _window_code(window))
     _check(lib().clear_attn_fwd_strip(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, d,
                                       n_text, grid_h, grid_w, ctypes.byref(opts), row_begin, row_end,
@@ -291,13 +297,23 @@ def text_merge(part_o, part_ml, out, n_text: int, grid_h: int, grid_w: int, mode
     modes = {"exact": CLEAR_MERGE_EXACT, "patch_average": CLEAR_MERGE_PATCH_AVERAGE}
     if mode not in modes:
         raise ValueError(f"mode must be one of {sorted(modes)}")
+    if out.dim() != 4:
+        raise ValueError("out must be [B, H, N, d]")
     B, H, N, d = out.shape
+    if N != n_text + grid_h * grid_w:
+        raise ValueError(f"N = {N} != n_text + grid_h * grid_w = {n_text + grid_h * grid_w}")
+    if out.dtype == torch.bfloat16:
+        dtype = CLEAR_BF16
+    elif out.dtype == torch.float32:
+        dtype = CLEAR_FP32
+    else:
+        raise TypeError(f"out must be bfloat16 or float32 (got {out.dtype})")
+    _expect(out, "out", out.device, out.dtype, out.shape)
+    if part_o.dim() != 4:
+        raise ValueError("part_o must be [P, B*H, n_text, d]")
     P = part_o.shape[0]
-    if tuple(part_o.shape) != (P, B * H, n_text, d) or tuple(part_ml.shape) != (P, B * H, n_text, 2):
-        raise ValueError("partials must be [P, B*H, n_text, d] and [P, B*H, n_text, 2]")
-    if not (part_o.is_contiguous() and part_ml.is_contiguous() and out.is_contiguous()):
-        raise ValueError("buffers must be contiguous")
-    dtype = CLEAR_BF16 if out.dtype == torch.bfloat16 else CLEAR_FP32
+    _expect(part_o, "part_o", out.device, torch.float32, (P, B * H, n_text, d))
+    _expect(part_ml, "part_ml", out.device, torch.float32, (P, B * H, n_text, 2))
     lse = torch.empty((B, H, N), dtype=torch.float32, device=out.device) if return_lse else None
     _check(lib().clear_text_merge(part_o.data_ptr(), part_ml.data_ptr(), P, modes[mode], out.data_ptr(),
                                   lse.data_ptr() if lse is not None else None, B, H, d, n_text, grid_h,
@@ -353,4 +369,29 @@ def tile_map_build_device(grid_h, grid_w, r2, tile_h=TILE_H, tile_w=TILE_W, sub_
         "offsets": off.cpu().numpy().view(np.uint32),
         "key_tiles": kt.cpu().numpy().view(np.uint32)[:n],
         "flags": fl.cpu().numpy().view(np.uint16)[:n],
+    }
+
+
+def tile_map_descriptors(grid_h, grid_w, r2, device="cuda", window: str = "circle"):
+    """The kernels' tile map built on the device with each entry's descriptor
+    (clear_tile_map_descriptors); returns numpy copies, ``desc`` as [n, 4] uint32."""
+    import torch
+
+    L = lib()
+    n = tile_map_size(grid_h, grid_w, r2, window=window)
+    nt = _ntiles(grid_h, grid_w, TILE_H, TILE_W)
+    off = torch.zeros(nt + 1, dtype=torch.int32, device=device)
+    kt = torch.zeros(max(n, 1), dtype=torch.int32, device=device)
+    fl = torch.zeros(max(n, 1), dtype=torch.int16, device=device)
+    desc = torch.zeros((max(n, 1), 4), dtype=torch.int32, device=device)
+    got = ctypes.c_size_t()
+    _check(L.clear_tile_map_descriptors(_window_code(window), grid_h, grid_w, r2, off.data_ptr(),
+                                        kt.data_ptr(), fl.data_ptr(), desc.data_ptr(), n, ctypes.byref(got),
+                                        _stream_of(off)))
+    torch.cuda.current_stream(off.device).synchronize()
+    return {
+        "offsets": off.cpu().numpy().view(np.uint32),
+        "key_tiles": kt.cpu().numpy().view(np.uint32)[:n],
+        "flags": fl.cpu().numpy().view(np.uint16)[:n],
+        "desc": desc.cpu().numpy().view(np.uint32)[:n],
     }

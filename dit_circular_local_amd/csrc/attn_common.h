@@ -3,10 +3,9 @@
 // the walk over a workgroup's chunks (dense token ranges, then the 4 x 8 cell
 // tiles the tile map lists for its tile) and the per-element window mask.
 //
-// The mask is CLEAR's (pith.science review of arXiv 2412.16112, "Core claim"):
-// a pair is admitted when either token is text or the two image cells are
-// within radius r; the square window of "What carries the argument" replaces
-// the distance by max(dy^2, dx^2).
+// The mask is CLEAR's (pith.science review of arXiv 2412.16112, "Core claim"),
+// 0-based: M_ij = [i < n_text] | [j < n_text] | [dy^2 + dx^2 <= r2]; the square
+// window of "What carries the argument" tests max(dy^2, dx^2) <= r2 instead.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -1,8 +1,8 @@
 // attn_fwd.hip -- fused CLEAR attention forward for gfx950 (MI355X).
 //
 // What is computed: masked softmax attention with CLEAR's circular-window mask
-// (pith.science review of arXiv 2412.16112, "Core claim": a pair is admitted
-// when either token is text or the two image tokens are within radius r), logits
+// (pith.science review of arXiv 2412.16112, "Core claim"; 0-based,
+// M_ij = [i < n_text] | [j < n_text] | [dy^2 + dx^2 <= r2]), logits
 // scaled by 1/sqrt(d) (the review's Eq. 1 / Eq. 7), text queries attending to
 // every key (the review's referee summary: text-token attention stays global).
 //

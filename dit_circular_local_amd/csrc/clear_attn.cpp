@@ -166,24 +166,27 @@ int choose_text_splits(int B, int H, int n_text, int N, int ntiles, size_t img_c
 // about to be enqueued on stream s.  If the previous user ran on another
 // stream, s first waits (on the device) for that user's kernels, so calls on
 // different streams take turns with the buffer; workspace_done records the
-// end of this call's use.  Caller holds g_mu.
+// end of this call's use.  Growth is stream-ordered and never blocks the host:
+// once s has waited for the last user, the old buffer is released with
+// hipFreeAsync on s and the new one taken with hipMallocAsync on s, so both
+// happen after every kernel that used the old buffer and before the kernels
+// of this call.  Caller holds g_mu.
 int workspace(DevState& ds, size_t need, hipStream_t s, void** out) {
+  hipError_t e;
+  if (ds.ws_done && ds.ws_stream != s) {
+    if ((e = hipStreamWaitEvent(s, ds.ws_done, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (workspace)");
+  }
   if (need > ds.ws_bytes) {
-    hipError_t e;
-    // the old workspace may still be read by queued kernels
     if (ds.ws) {
-      if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-      (void)hipFree(ds.ws);
+      if ((e = hipFreeAsync(ds.ws, s)) != hipSuccess) return hip_fail(e, "hipFreeAsync (workspace)");
       ds.ws = nullptr;
       ds.ws_bytes = 0;
     }
-    if ((e = hipMalloc(&ds.ws, need)) != hipSuccess)
+    if ((e = hipMallocAsync(&ds.ws, need, s)) != hipSuccess) {
+      ds.ws = nullptr;
       return set_error(CLEAR_ENOMEM, "workspace (%zu bytes): %s", need, hipGetErrorString(e));
+    }
     ds.ws_bytes = need;
-  }
-  if (ds.ws_done && ds.ws_stream != s) {
-    hipError_t e = hipStreamWaitEvent(s, ds.ws_done, 0);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (workspace)");
   }
   *out = ds.ws;
   return CLEAR_OK;
@@ -230,7 +233,7 @@ using namespace clear;
 
 extern "C" const char* clear_last_error(void) { return g_err; }
 
-extern "C" int clear_version(void) { return 10300; }
+extern "C" int clear_version(void) { return 10400; }
 
 namespace {
 
@@ -525,6 +528,35 @@ extern "C" int clear_tile_map_build_device_ex(int window, int grid_h, int grid_w
   return CLEAR_OK;
 }
 
+extern "C" int clear_tile_map_descriptors(int window, int grid_h, int grid_w, int r2_max, uint32_t* offsets,
+                                          uint32_t* key_tiles, uint16_t* flags, uint32_t* desc, size_t cap,
+                                          size_t* n_entries, void* stream) {
+  clear_error_reset();
+  if (window != CLEAR_WINDOW_CIRCLE && window != CLEAR_WINDOW_SQUARE)
+    return set_error(CLEAR_EINVAL, "window must be CLEAR_WINDOW_CIRCLE or CLEAR_WINDOW_SQUARE (got %d)",
+                     window);
+  int rc = tile_map_validate(grid_h, grid_w, r2_max, CLEAR_TILE_H, CLEAR_TILE_W, CLEAR_SUB_H, CLEAR_SUB_W,
+                             CLEAR_KEY_H, CLEAR_KEY_W);
+  if (rc) return rc;
+  if (!n_entries) return set_error(CLEAR_EINVAL, "n_entries must not be NULL");
+  TileGeom g = make_geom(grid_h, grid_w, r2_max, CLEAR_TILE_H, CLEAR_TILE_W, CLEAR_SUB_H, CLEAR_SUB_W,
+                         CLEAR_KEY_H, CLEAR_KEY_W, window);
+  *n_entries = tile_map_count(g);
+  rc = tile_map_check_entries(*n_entries);
+  if (rc) return rc;
+  if (*n_entries > cap)
+    return set_error(CLEAR_ENOMEM, "tile map needs %zu entries (capacity %zu)", *n_entries, cap);
+  if (!offsets || (*n_entries && (!key_tiles || !flags || !desc)))
+    return set_error(CLEAR_EINVAL, "tile map output pointers must not be NULL");
+  rc = tile_map_build_device_launch(g, offsets, key_tiles, flags, desc, stream);
+  if (rc) return rc;
+  if (debug_sync_enabled()) {
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "CLEAR_DEBUG sync");
+  }
+  return CLEAR_OK;
+}
+
 extern "C" int clear_tile_map_build_device(int grid_h, int grid_w, int r2_max, int tile_h, int tile_w,
                                            int sub_h, int sub_w, int key_h, int key_w, uint32_t* offsets,
                                            uint32_t* key_tiles, uint16_t* flags, size_t cap,
@@ -548,7 +580,10 @@ extern "C" void clear_release_cache(void) {
       delete m.second.mask_host;
     }
     kv.second.maps.clear();
-    if (kv.second.ws) (void)hipFree(kv.second.ws);
+    if (kv.second.ws) {
+      (void)hipFreeAsync(kv.second.ws, nullptr);
+      (void)hipDeviceSynchronize();
+    }
     kv.second.ws = nullptr;
     kv.second.ws_bytes = 0;
     if (kv.second.ws_done) (void)hipEventDestroy(kv.second.ws_done);

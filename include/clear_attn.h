@@ -30,10 +30,15 @@
  *     the problem.  Argument checks run before any HIP call.
  *   - Device pointers are plain addresses in the current HIP device's memory.
  *     `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
- *     work is enqueued on that stream; the library never synchronises it
- *     (except where stated, and when the environment variable CLEAR_DEBUG=1
- *     is set, which synchronises after each launch and maps failures to
- *     CLEAR_EHIP).
+ *     work is enqueued on that stream; the library never synchronises it.
+ *     Exceptions: clear_release_cache (synchronises every device it used);
+ *     the clean-up after a failed HIP call while a tile map is being built
+ *     (synchronises the stream before freeing); and CLEAR_DEBUG=1 in the
+ *     environment, which synchronises after each launch and maps failures to
+ *     CLEAR_EHIP.  The library's workspace grows in stream order: the old
+ *     buffer is released with hipFreeAsync and the new one taken with
+ *     hipMallocAsync on the caller's stream, after that stream has waited for
+ *     the buffer's previous user, so growth never blocks the host.
  *   - Faults inside kernels surface at the caller's next synchronisation.
  *   - Thread safety: every entry point may be called from several host
  *     threads; the library's caches are guarded by a mutex.  Calls that use
@@ -286,6 +291,35 @@ int clear_tile_map_build_device_ex(int window, int grid_h, int grid_w, int r2_ma
                                    int key_w, uint32_t* offsets, uint32_t* key_tiles,
                                    uint16_t* flags, size_t cap, size_t* n_entries,
                                    void* stream);
+
+/*
+ * clear_tile_map_descriptors -- the tile map at the attention kernels' own tiling
+ * (CLEAR_TILE_H x CLEAR_TILE_W query tiles, CLEAR_SUB_H x CLEAR_SUB_W sub-tiles,
+ * CLEAR_KEY_H x CLEAR_KEY_W key tiles), built on `stream` by the same kernels and
+ * launch that build the layer entry points' cached copy, together with each
+ * entry's descriptor, which the attention kernels read in place of the list.
+ * Exposed so that the descriptors can be checked against the list they are
+ * derived from (added in 1.4).
+ *   window, grid_h, grid_w, r2_max, offsets, key_tiles, flags, cap, n_entries:
+ *     as clear_tile_map_build_device_ex at that tiling (offsets, key_tiles and
+ *     flags device buffers; n_entries a host pointer).
+ *   desc : device, [cap][4] uint32, caller-owned.  For entry e with key tile
+ *          (ky, kx) = divmod(key_tiles[e], ceil(grid_w / CLEAR_KEY_W)):
+ *            desc[e][0] = ky*CLEAR_KEY_H*grid_w + kx*CLEAR_KEY_W, the token
+ *                         offset of the key tile's first cell from the first
+ *                         image token;
+ *            desc[e][1] = flags[e] | (1 << 16) when the key tile lies wholly on
+ *                         the grid, else flags[e];
+ *            desc[e][2] = (ky << 16) | kx;
+ *            desc[e][3] = grid_h*grid_w - desc[e][0], the image tokens from the
+ *                         first cell to the end of the grid.
+ * Errors as clear_tile_map_build_device_ex (CLEAR_ENOMEM with *n_entries set
+ * when cap is too small; nothing launched); desc must not be NULL when the map
+ * has entries.
+ */
+int clear_tile_map_descriptors(int window, int grid_h, int grid_w, int r2_max,
+                               uint32_t* offsets, uint32_t* key_tiles, uint16_t* flags,
+                               uint32_t* desc, size_t cap, size_t* n_entries, void* stream);
 
 /* Message of the last error raised on the calling thread ("" if none). */
 const char* clear_last_error(void);

@@ -8,9 +8,9 @@ share no code.
 
 What it computes comes from the pages about CLEAR (arXiv 2412.16112):
 
-* the attention mask M of the pith.science review of the paper ("Core claim"):
-  a pair (i, j) is admitted when either token is a text token or the two image
-  tokens lie within Euclidean radius r on the token grid;
+* the attention mask of the pith.science review of the paper ("Core claim"),
+  written here 0-based as M_ij = [i < n_text] or [j < n_text] or
+  [dy_ij^2 + dx_ij^2 <= r2], with (dy, dx) the grid offset of two image tokens;
 * plain softmax attention with 1/sqrt(c) logit scaling (the same review,
   "Assumptions & free parameters": Eq. 1; "What carries the argument": Eq. 7);
 * text queries attend to every key (the review's referee summary: text-token
@@ -31,10 +31,12 @@ backward   -- its gradients by the chain rule (full layer, chosen query rows or 
 tilemap    -- tile lists (key tiles per query tile, sub-tile flags) by brute force
 counts     -- lattice-point and admitted-pair counts by enumeration
 
-Parity status: every function here has at least one pin in
-``tests/test_oracle_pins.py``, ``tests/test_oracle_tilemap.py``,
-``tests/test_oracle_square.py``, ``tests/test_oracle_strips.py`` or
-``tests/test_oracle_backward.py``.
+Parity status: every exported function has at least one pin against values
+the pages or plain mathematics fix (closed forms, library routines, brute
+force, finite differences), in ``tests/test_oracle_pins.py`` (attention,
+counts and the admitted-pair counter ``in_window_pairs``),
+``tests/test_oracle_tilemap.py``, ``tests/test_oracle_square.py``,
+``tests/test_oracle_strips.py`` or ``tests/test_oracle_backward.py``.
 """
 
 from .attention import (  # noqa: F401

@@ -202,6 +202,14 @@ def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_text: int,
     return out, lse
 
 
+def _one_blas_thread():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:  # threadpoolctl missing: keep the library default
+        pass
+
+
 def _head_job(args):
     qh, kh, vh, n_text, grid_h, grid_w, r2, block, window = args
     return attention_head(qh, kh, vh, n_text, grid_h, grid_w, r2, block, window=window)
@@ -221,8 +229,9 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_text: int,
             for b in range(B) for h in range(H)]
     if workers > 1 and len(jobs) > 1:
         import multiprocessing as mp
-        # fresh interpreters: the caller may hold a GPU context, which must not be forked
-        with mp.get_context("spawn").Pool(min(workers, len(jobs))) as pool:
+        # fresh interpreters: the caller may hold a GPU context, which must not be
+        # forked; one BLAS thread per worker, so the pool does not oversubscribe
+        with mp.get_context("spawn").Pool(min(workers, len(jobs)), initializer=_one_blas_thread) as pool:
             res = pool.map(_head_job, jobs)
     else:
         res = [_head_job(j) for j in jobs]

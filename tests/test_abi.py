@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert ca.version() == 10300  # 1.3.0: gradients (clear_attn_bwd)
+    assert ca.version() == 10400  # 1.4.0: tile-map descriptors exported (clear_tile_map_descriptors)
 
 
 # fake, aligned, non-overlapping device addresses: validation must fail before use
@@ -124,3 +124,123 @@ def _bwd(dtype=0, r2=4, lse_out=None, splits=0, window=0, q=Q, k=K, v=V, o=O, do
 def test_bwd_rejects_bad_arguments(kw, frag):
     assert _bwd(**kw) == ca.CLEAR_EINVAL
     assert frag in ca.last_error()
+
+
+# ---------------------------------------------------------------- binding checks
+# The binding must refuse buffers the C ABI cannot check (a host tensor, a
+# tensor on another device, a too-small element type) before any launch.  These
+# run without a GPU: a stand-in tensor reports CUDA placement and raises if the
+# binding ever asks for its address.
+
+class _FakeGpuTensor:
+    def __init__(self, shape, dtype, device="cuda:0", is_cuda=True, contiguous=True):
+        import torch
+        self.shape = tuple(shape)
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.is_cuda = is_cuda
+        self._contig = contiguous
+
+    def dim(self):
+        return len(self.shape)
+
+    def is_contiguous(self):
+        return self._contig
+
+    def data_ptr(self):
+        raise AssertionError("the binding reached a launch with a bad buffer")
+
+    def element_size(self):
+        return 2
+
+
+def _qkv(dtype=None, shape=(1, 2, 8 + 16, 64)):
+    import torch
+    dtype = dtype or torch.bfloat16
+    return tuple(_FakeGpuTensor(shape, dtype) for _ in range(3))
+
+
+def test_binding_fwd_rejects_bad_out_before_launch():
+    import torch
+    q, k, v = _qkv()
+    bad = [
+        _FakeGpuTensor(q.shape, torch.bfloat16, device="cpu", is_cuda=False),   # host tensor
+        _FakeGpuTensor(q.shape, torch.bfloat16, device="cuda:1"),               # other device
+        _FakeGpuTensor(q.shape, torch.float16),                                 # wrong dtype
+        _FakeGpuTensor((1, 2, 8 + 16, 32), torch.bfloat16),                     # wrong shape
+        _FakeGpuTensor(q.shape, torch.bfloat16, contiguous=False),
+    ]
+    for out in bad:
+        with pytest.raises((ValueError, TypeError)):
+            ca.fwd(q, k, v, 8, 4, 4, radius=2, out=out)
+    k2 = _FakeGpuTensor(q.shape, torch.bfloat16, device="cuda:1")
+    with pytest.raises(ValueError):
+        ca.fwd(q, k2, v, 8, 4, 4, radius=2, out=_FakeGpuTensor(q.shape, torch.bfloat16))
+
+
+def test_binding_bwd_rejects_bad_buffers_before_launch():
+    import torch
+    q, k, v = _qkv()
+    B, H, N, d = q.shape
+    good = dict(out=_FakeGpuTensor(q.shape, torch.bfloat16), dout=_FakeGpuTensor(q.shape, torch.bfloat16),
+                lse=_FakeGpuTensor((B, H, N), torch.float32))
+    grads = tuple(_FakeGpuTensor(q.shape, torch.bfloat16) for _ in range(3))
+    cases = [
+        dict(good, lse=_FakeGpuTensor((B, H, N), torch.bfloat16)),
+        dict(good, lse=_FakeGpuTensor((B, H, N), torch.float32, device="cpu", is_cuda=False)),
+        dict(good, dout=_FakeGpuTensor(q.shape, torch.float32)),
+        dict(good, out=_FakeGpuTensor(q.shape, torch.bfloat16, device="cuda:3")),
+    ]
+    for c in cases:
+        with pytest.raises((ValueError, TypeError)):
+            ca.bwd(q, k, v, c["out"], c["dout"], c["lse"], 8, 4, 4, radius=2, grads=grads)
+    for i in range(3):
+        g = list(grads)
+        g[i] = _FakeGpuTensor(q.shape, torch.bfloat16, device="cpu", is_cuda=False)
+        with pytest.raises(ValueError):
+            ca.bwd(q, k, v, good["out"], good["dout"], good["lse"], 8, 4, 4, radius=2, grads=tuple(g))
+
+
+def test_binding_strip_and_merge_reject_bad_partials_before_launch():
+    import torch
+    q, k, v = _qkv()
+    B, H, N, d = q.shape
+    out = _FakeGpuTensor(q.shape, torch.bfloat16)
+    po = _FakeGpuTensor((B * H, 8, d), torch.float32)
+    pml = _FakeGpuTensor((B * H, 8, 2), torch.float32)
+    for bad_o, bad_ml in [(_FakeGpuTensor((B * H, 8, d), torch.bfloat16), pml),
+                          (po, _FakeGpuTensor((B * H, 8, 2), torch.float16)),
+                          (_FakeGpuTensor((B * H, 8, d), torch.float32, device="cpu", is_cuda=False), pml)]:
+        with pytest.raises((ValueError, TypeError)):
+            ca.fwd_strip(q, k, v, 8, 4, 4, 0, 2, out, bad_o, bad_ml, radius=2)
+    with pytest.raises((ValueError, TypeError)):
+        ca.fwd_strip(q, k, v, 8, 4, 4, 0, 2, _FakeGpuTensor(q.shape, torch.float32), po, pml, radius=2)
+    P = 3
+    po3 = _FakeGpuTensor((P, B * H, 8, d), torch.float32)
+    pml3 = _FakeGpuTensor((P, B * H, 8, 2), torch.float32)
+    merge_cases = [
+        (_FakeGpuTensor(q.shape, torch.float16), po3, pml3),          # fp16 out: 4-byte writes would overrun
+        (out, _FakeGpuTensor((P, B * H, 8, d), torch.bfloat16), pml3),
+        (out, po3, _FakeGpuTensor((P, B * H, 8, 2), torch.float32, device="cuda:2")),
+        (out, _FakeGpuTensor((P, B * H, 8, d), torch.float32, device="cpu", is_cuda=False), pml3),
+        (_FakeGpuTensor(q.shape, torch.bfloat16, device="cpu", is_cuda=False), po3, pml3),
+    ]
+    for o, a, b in merge_cases:
+        with pytest.raises((ValueError, TypeError)):
+            ca.text_merge(a, b, o, 8, 4, 4)
+
+
+def test_descriptor_builder_checks_before_launch():
+    L = ca.lib()
+    n = ctypes.c_size_t()
+    # capacity too small: size reported, nothing launched
+    assert L.clear_tile_map_descriptors(0, 64, 64, 64, None, None, None, None, 0, ctypes.byref(n),
+                                        None) == ca.CLEAR_ENOMEM
+    assert n.value == ca.tile_map_size(64, 64, 64)
+    assert L.clear_tile_map_descriptors(2, 64, 64, 64, None, None, None, None, 0, ctypes.byref(n),
+                                        None) == ca.CLEAR_EINVAL
+    assert L.clear_tile_map_descriptors(0, 0, 64, 64, None, None, None, None, 0, ctypes.byref(n),
+                                        None) == ca.CLEAR_EINVAL
+    assert L.clear_tile_map_descriptors(0, 64, 64, 64, 0x1000, 0x2000, 0x3000, None, n.value,
+                                        ctypes.byref(n), None) == ca.CLEAR_EINVAL
+    assert "NULL" in ca.last_error()

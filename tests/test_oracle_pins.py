@@ -297,3 +297,54 @@ def test_pages_reduction_and_speedup_figures():
     # if text queries saw only text (not the review's reading), 8K r=8 would read 99.7
     alt = c["img_img"] + c["img_text"] + n_text * n_text
     assert round(100.0 * (1.0 - alt / c["dense"]), 1) == 99.7
+
+
+# ---------------------------------------------------------------- in_window_pairs
+# The oracle's pair counter converts a timed sample of oracle rows into
+# in-window FLOPs.  Pinned against the separable closed form (pair_count, itself
+# pinned to the mask sum above), against direct mask sums of the sampled rows,
+# and by additivity over disjoint row subsets.
+
+@pytest.mark.parametrize("window", ["circle", "square"])
+@pytest.mark.parametrize("n_text,gh,gw,r2,block", [
+    (3, 9, 13, 5, 4), (0, 8, 8, 0, 8), (5, 17, 6, 20, 8), (2, 10, 10, -1, 4), (4, 7, 11, 1000, 3)])
+def test_in_window_pairs_whole_layer_equals_closed_form(window, n_text, gh, gw, r2, block):
+    from oracle import in_window_pairs
+
+    assert in_window_pairs(n_text, gh, gw, r2, block=block, window=window) == \
+        pair_count(n_text, gh, gw, r2, window)["total"]
+
+
+@pytest.mark.parametrize("window", ["circle", "square"])
+def test_in_window_pairs_subset_equals_mask_sum_of_its_rows(window):
+    """A chosen set of text rows and image blocks: the count equals the mask
+    summed over exactly those query rows and every key."""
+    from oracle import in_window_pairs
+
+    n_text, gh, gw, r2, block = 6, 19, 14, 18, 4
+    n = n_text + gh * gw
+    text_rows = [0, 2, 5]
+    blocks = [(0, 0), (2, 3), (4, 1), (4, 3)]  # includes the clipped bottom-right block
+    rows = list(text_rows)
+    for by, bx in blocks:
+        for y in range(by * block, min(gh, by * block + block)):
+            for x in range(bx * block, min(gw, bx * block + block)):
+                rows.append(n_text + y * gw + x)
+    want = int(clear_mask(rows, range(n), n_text, gw, r2, window).sum())
+    assert in_window_pairs(n_text, gh, gw, r2, text_rows=text_rows, blocks=blocks, block=block,
+                           window=window) == want
+
+
+def test_in_window_pairs_is_additive_over_disjoint_subsets():
+    from oracle import in_window_pairs
+
+    n_text, gh, gw, r2, block = 7, 16, 24, 50, 8
+    nby, nbx = -(-gh // block), -(-gw // block)
+    all_blocks = [(by, bx) for by in range(nby) for bx in range(nbx)]
+    a = in_window_pairs(n_text, gh, gw, r2, text_rows=[0, 1, 2], blocks=all_blocks[::2], block=block)
+    b = in_window_pairs(n_text, gh, gw, r2, text_rows=[3, 4, 5, 6], blocks=all_blocks[1::2], block=block)
+    assert a + b == pair_count(n_text, gh, gw, r2)["total"]
+    # an empty subset counts nothing; text rows alone count N each
+    assert in_window_pairs(n_text, gh, gw, r2, text_rows=[], blocks=[], block=block) == 0
+    assert in_window_pairs(n_text, gh, gw, r2, text_rows=[1, 4], blocks=[], block=block) == \
+        2 * (n_text + gh * gw)

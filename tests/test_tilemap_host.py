@@ -120,3 +120,13 @@ def test_maps_beyond_32_bit_offsets_are_rejected():
     assert rc == ca.CLEAR_ENOTSUP and got.value == n
     assert not off.any()
     assert "32-bit" in ca.lib().clear_last_error().decode()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("g", [128, 256, 512])
+@pytest.mark.parametrize("r", [8, 16, 32])
+def test_flux_grids_whole_map_against_bruteforce(g, r):
+    """The 2048^2 / 4096^2 / 8192^2 token grids (128^2, 256^2, 512^2 cells) at the
+    pages' radii: the kernels' whole tile map, every query tile and every flag,
+    against the oracle's pair-by-pair brute force (candidate box only)."""
+    _same(ca.tile_map_build(g, g, r * r), tile_map_bruteforce(g, g, r * r, box=True))

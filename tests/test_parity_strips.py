@@ -119,3 +119,62 @@ def test_strip_and_merge_reject_bad_arguments():
     rc = L.clear_text_merge(po.data_ptr(), pml.data_ptr(), 0, ca.CLEAR_MERGE_EXACT, out.data_ptr(),
                             None, 1, 1, d, n_text, gh, gw, ca.CLEAR_BF16, None)
     assert rc == ca.CLEAR_EINVAL
+
+
+def _slab(t, n_text, gw, lo, hi):
+    """Text tokens plus image rows [lo, hi) of [B, H, N, d] t, as a contiguous
+    buffer: what one device of a patch-parallel run holds."""
+    idx = torch.cat([torch.arange(n_text), n_text + torch.arange(lo * gw, hi * gw)]).to(t.device)
+    return t.index_select(2, idx).contiguous()
+
+
+@pytest.mark.parametrize("gh,gw,H,r,P", [(128, 128, 2, 16, 4), (128, 64, 2, 8, 8), (512, 512, 1, 32, 8),
+                                         (80, 24, 3, 5, 5)])
+def test_slab_local_strips_equal_the_layer(gh, gw, H, r, P):
+    """Each strip computed on a buffer holding only the text tokens, its own rows
+    and halos of h rows above and below (h = isqrt(r2) rounded up to the
+    16-row query-tile height, clipped at the grid's edges): the O(r x W) slab of
+    one device in the pages' patch-parallel inference (pith.science review of
+    CLEAR, "What carries the argument").  With the strip's local grid and row
+    range, its image rows equal the whole layer's bit for bit, its text-row
+    partial equals the one computed on the full-size tensors, and the exact
+    merge of the slabs' partials gives the text rows of the layer."""
+    n_text, d, r2 = 512, 128, r * r
+    q, k, v = _inputs("bf16", 1, H, n_text, gh, gw, d, seed=gh + r)
+    full = ca.fwd(q, k, v, n_text, gh, gw, r2=r2)
+    h = -(-math.isqrt(r2) // 16) * 16
+    rows = [(y0, y1) for y0, y1 in ca.strip_rows(gh, P)]
+    assert all(y0 % 16 == 0 for y0, _ in rows) or gh == 80
+    po = torch.zeros((P, H, n_text, d), dtype=torch.float32, device="cuda")
+    pml = torch.zeros((P, H, n_text, 2), dtype=torch.float32, device="cuda")
+    po_full, pml_full = torch.zeros_like(po), torch.zeros_like(pml)
+    out_full = torch.zeros_like(q)
+    merged = torch.zeros_like(q)
+    for s, (y0, y1) in enumerate(rows):
+        lo, hi = max(0, y0 - h), min(gh, y1 + h)
+        ql, kl, vl = (_slab(t, n_text, gw, lo, hi) for t in (q, k, v))
+        outl = torch.zeros_like(ql)
+        ca.fwd_strip(ql, kl, vl, n_text, hi - lo, gw, y0 - lo, y1 - lo, outl, po[s], pml[s], r2=r2,
+                     with_text_keys=(s == 0))
+        ca.fwd_strip(q, k, v, n_text, gh, gw, y0, y1, out_full, po_full[s], pml_full[s], r2=r2,
+                     with_text_keys=(s == 0))
+        torch.cuda.synchronize()
+        mine = outl[:, :, n_text + (y0 - lo) * gw:n_text + (y1 - lo) * gw]
+        if (y0 - lo) % 16 == 0 and lo % 16 == 0:
+            # the slab's query tiles are the layer's: same chunk lists, same order
+            assert torch.equal(mine, full[:, :, n_text + y0 * gw:n_text + y1 * gw]), f"strip {s}"
+        else:
+            # a slab cut off the 16-row tiling groups the queries differently
+            err = (mine.float() - full[:, :, n_text + y0 * gw:n_text + y1 * gw].float()).abs().max().item()
+            assert err <= 2e-2, f"strip {s}: max-abs {err:.3e}"
+        assert torch.equal(po[s], po_full[s]) and torch.equal(pml[s], pml_full[s]), f"strip {s} partial"
+    ca.text_merge(po, pml, merged, n_text, gh, gw, mode="exact")
+    torch.cuda.synchronize()
+    ref, _ = attention(_np(q[:, :, :]), _np(k), _np(v), n_text, gh, gw, r2, workers=8) if gh * gw <= 16384 \
+        else (None, None)
+    if ref is not None:
+        err = np.abs(_np(merged[:, :, :n_text]) - ref[:, :, :n_text]).max()
+        assert err <= TOL["bf16"], f"text rows: max-abs {err:.3e}"
+    else:
+        err = (merged[:, :, :n_text].float() - full[:, :, :n_text].float()).abs().max().item()
+        assert err <= TOL["bf16"], f"text rows vs the layer: max-abs {err:.3e}"

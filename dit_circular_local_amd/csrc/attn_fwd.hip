@@ -43,7 +43,6 @@
 namespace clear {
 namespace {
 
-constexpr int kStages = 2;
 constexpr int kTextQ = kWaves * 32;  // text queries per workgroup
 constexpr float kLazyTau = 8.0f;
 constexpr float kMInit = -1.0e30f;
@@ -88,6 +87,7 @@ struct Bf16 {
   static constexpr int kKK = D / 16;
   static constexpr int kNB = D / 32;
   static constexpr int kWavesPerSimd = 3;
+  static constexpr int kStages = 2;
 
   static constexpr int kRowK = kSlotsK * 16;
   static constexpr int kRowV = kSlotsV * 16;
@@ -182,6 +182,123 @@ struct Bf16 {
   }
 };
 
+// bf16 inputs at d = 128.  K and V sit in LDS in copy
+// blocks: one direct-to-LDS copy of a wavefront (64 lanes x 16 bytes) fills one
+// 1 KB block holding four whole 256-byte rows.  A row is four 64-byte granules
+// (four 16-byte pieces each); within a block, granule c of row j sits at
+// bytes 256 c + 64 j, so lane l of the copy reads granule l / 16 of row
+// (l / 4) % 4, piece l % 4 of it: every four consecutive lanes read 64
+// contiguous bytes of global memory.  Consecutive blocks start one 16-byte
+// bank group further round the LDS (pitch 1040 bytes), so that
+//  * the row-per-lane K reads (ds_read_b128, eight or sixteen consecutive
+//    rows, one piece index) hit distinct bank groups: 4 j + v within a
+//    block, plus the block's skew;
+//  * the V transpose reads (ds_read_b64_tr_b16: per 16-lane group four rows of
+//    a block, two pieces each) read 128 distinct bytes;
+//  * a piece's offset from the row's first piece is the same on every lane
+//    (256 bytes per granule, 16 per piece), so one lane address and
+//    immediate offsets serve every product.
+// No slot is padding: a chunk is 16 copies (4 per wavefront), 16 KB of LDS
+// writes, where a row pitch of 17 or 20 slots takes 24.
+struct Bf16G {
+  static constexpr int D = 128;
+  static constexpr int kElem = 2;
+  static constexpr int kRowBytes = D * 2;          // global row
+  static constexpr int kRowsPerBlock = 4;
+  static constexpr int kBlocks = kChunk / kRowsPerBlock;  // copy blocks per region (K or V)
+  static constexpr int kBlocksPerWave = kBlocks / kWaves;
+  static constexpr int kPitch = 1024 + 16;         // block pitch: one bank group of skew
+  static constexpr int kKK = D / 16;
+  static constexpr int kNB = D / 32;
+  static constexpr int kWavesPerSimd = 3;
+  static constexpr int kStages = 2;
+  static constexpr int kKOff = 0;
+  static constexpr int kVOff = kBlocks * kPitch;
+  static constexpr int kStage = 2 * kBlocks * kPitch;
+  static_assert(kBlocks % kWaves == 0, "copy blocks split evenly over the wavefronts");
+
+  // LDS byte offset, within a region, of element `col` of chunk row `row`
+  __device__ static constexpr int lds_off(int row, int col) {
+    return (row / 4) * kPitch + 256 * (col / 32) + 64 * (row % 4) + 16 * ((col / 8) % 4) + 2 * (col % 8);
+  }
+
+  bf16x8_t q[kKK];
+  f32x16_t o[kNB];
+
+  __device__ void load_q(const char* qrow, bool valid, int g) {
+    for (int kk = 0; kk < kKK; ++kk) {
+      const u32x4_t x = *(const u32x4_t*)(qrow + (16 * kk + 8 * g) * 2);
+      q[kk] = __builtin_bit_cast(bf16x8_t, valid ? x : u32x4_t{0, 0, 0, 0});
+    }
+  }
+  __device__ void zero_o() {
+    for (int nb = 0; nb < kNB; ++nb) o[nb] = f32x16_t{};
+  }
+  __device__ void scale_o(float a) {
+    for (int nb = 0; nb < kNB; ++nb)
+      for (int i = 0; i < 16; ++i) o[nb][i] *= a;
+  }
+  __device__ void settle_q() {
+    for (int kk = 0; kk < kKK; ++kk) asm volatile("" ::"v"(q[kk]));
+  }
+  // K rows: lane l reads row l % 32, piece 2 kk + l / 32 (d values
+  // 16 kk + 8 (l / 32) .. + 7) for product kk: granule kk / 2, piece
+  // 2 (kk % 2) + l / 32 within it.
+  __device__ void qk(const char* st, int lane, f32x16_t& s, const f32x16_t& init) const {
+    const char* kb = st + kKOff + lds_off(lane & 31, 8 * (lane >> 5));
+    s = init;
+    for (int kk = 0; kk < kKK; ++kk) {
+      bf16x8_t a = *(const bf16x8_t*)(kb + 256 * (kk / 2) + 32 * (kk % 2));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q[kk], s, 0, 0, 0);
+      // at most four operands in flight (register budget of three waves per SIMD)
+      if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  struct Probs {
+    bf16x8_t b[2];
+  };
+  __device__ static void probs(const f32x16_t& e, Probs& pr, float& l) {
+    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+    for (int t = 0; t < 2; ++t)
+      for (int j = 0; j < 4; ++j) {
+        const bf16x2_t h = __builtin_convertvector(f32x2_t{e[8 * t + 2 * j], e[8 * t + 2 * j + 1]}, bf16x2_t);
+        pr.b[t][2 * j] = h[0];
+        pr.b[t][2 * j + 1] = h[1];
+        l = __builtin_amdgcn_fdot2_f32_bf16(h, one, l, false);
+      }
+  }
+  // O^T += V^T P^T, the A operand from transpose loads as in the padded
+  // engine: lane s of a 16-lane group addresses key row 16t + 8h + 4g + s/4 at
+  // columns 32nb + 16 ((l/16) % 2) + 4 (s % 4).  Rows 16t + 8h further are
+  // 4t + 2h blocks further, columns 32nb further one granule (256 bytes)
+  // further, so the lane address of (t, h, nb) = (0, 0, 0) serves all.
+  __device__ void pv(const char* st, int lane, const Probs& pr) {
+    const int g = lane >> 5;
+    const int s = lane & 15;
+    const int half = (lane >> 4) & 1;
+    const char* vb = st + kVOff + lds_off(4 * g + (s >> 2), 16 * half + 4 * (s & 3));
+    for (int t = 0; t < 2; ++t) {
+      for (int nb = 0; nb < kNB; ++nb) {
+        const char* a0 = vb + 4 * t * kPitch + 256 * nb;
+        s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds_char_t*)const_cast<char*>(a0));
+        s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(lds_char_t*)const_cast<char*>(a0 + 2 * kPitch));
+        s16x8_t w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pr.b[t], o[nb], 0, 0, 0);
+        if (nb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  __device__ static void store4(char* dst, float a, float b, float c, float d) {
+    bf16x2_t h0 = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
+    bf16x2_t h1 = __builtin_convertvector(f32x2_t{c, d}, bf16x2_t);
+    uint2 w;
+    w.x = __builtin_bit_cast(unsigned, h0);
+    w.y = __builtin_bit_cast(unsigned, h1);
+    *(uint2*)dst = w;
+  }
+};
+
 // fp32 inputs; K and V row-major in LDS.
 template <int D>
 struct F32 {
@@ -193,6 +310,7 @@ struct F32 {
   static constexpr int kHalf = D / 2;   // d values per lane group in Q.K
   static constexpr int kNB = D / 32;
   static constexpr int kWavesPerSimd = 1;
+  static constexpr int kStages = 2;
 
   static constexpr int kRowK = kSlotsK * 16;
   static constexpr int kRowV = kSlotsV * 16;
@@ -326,6 +444,75 @@ __device__ __forceinline__ void stage_chunk(char* st, const ChunkMeta& m, bool d
   }
 }
 
+// ------------------------------------------- copies of the bf16 block layout
+
+// Copy plan of the granule layout (Bf16G): lane l of wavefront w fills slot l
+// of blocks w + 4i (i < kBlocksPerWave) of both regions, i.e. piece
+// 4 (l / 16) + l % 4 of chunk row 4 (w + 4i) + (l / 4) % 4.  Its byte offsets
+// from the chunk's first key: for a dense token range (consecutive rows) and
+// for a key tile (row 8a + c is cell (a, c), rows a grid row, gw tokens,
+// apart).  K and V use the same offsets.
+template <class E>
+struct BlockPlan {
+  uint32_t dense[E::kBlocksPerWave], tile[E::kBlocksPerWave];
+};
+
+template <class E>
+__device__ __forceinline__ BlockPlan<E> make_block_plan(int wave, int lane, int gw) {
+  BlockPlan<E> pl;
+  for (int i = 0; i < E::kBlocksPerWave; ++i) {
+    const int r = E::kRowsPerBlock * (wave + kWaves * i) + (lane >> 2) % E::kRowsPerBlock;
+    const int pc = 4 * (lane >> 4) + (lane & 3);
+    pl.dense[i] = (uint32_t)(r * E::kRowBytes + pc * 16);
+    pl.tile[i] = (uint32_t)(((r >> 3) * gw + (r & 7)) * E::kRowBytes + pc * 16);
+  }
+  return pl;
+}
+
+// Buffer resource words (gfx9 layout, stride 0) over `bytes` bytes from a
+// uniform address: offsets at or past `bytes` read zeros.
+__device__ __forceinline__ u32x4_t rsrc_words(const char* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// One wavefront's direct-to-LDS copy of 64 x 16 bytes: lane l's piece at byte
+// voff of the resource lands at LDS address lds + 16 l.  Written in assembly so
+// that the compiler does not take it for a writer of the stage being read (it
+// cannot tell the two stages apart and would wait for the next chunk's copies
+// before the V reads of the current one); the walk waits for the copies
+// itself, before each barrier (stage_barrier).
+__device__ __forceinline__ void lds_copy(uint32_t lds, const u32x4_t& rsrc, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(lds_char_t*)const_cast<char*>(p);
+}
+
+// Start the copy of a chunk into stage st (kCopies copies per wavefront, the
+// same on every path) in the granule layout.  The resources start at the chunk's first key and end
+// with the head: pieces past the head read zeros, pieces past the grid's right
+// edge or a dense range's limit read other real keys, all masked.
+template <class E>
+__device__ __forceinline__ void stage_blocks(char* st, const ChunkMeta& m, bool dense, int wave,
+                                             const char* kbase, const char* vbase, const BlockPlan<E>& pl) {
+  const size_t off = (size_t)m.tok0 * E::kRowBytes;
+  constexpr int kMaxLeft = 0x7fffffff / E::kRowBytes;  // a resource covers < 2 GB
+  const uint32_t bytes = (uint32_t)(m.left < kMaxLeft ? m.left : kMaxLeft) * E::kRowBytes;
+  const u32x4_t rk = rsrc_words(kbase + off, bytes), rv = rsrc_words(vbase + off, bytes);
+  const uint32_t sk = lds_addr(st) + E::kKOff + wave * E::kPitch;
+  const uint32_t sv = lds_addr(st) + E::kVOff + wave * E::kPitch;
+  if (dense) {
+    for (int i = 0; i < E::kBlocksPerWave; ++i) lds_copy(sk + i * kWaves * E::kPitch, rk, pl.dense[i]);
+    for (int i = 0; i < E::kBlocksPerWave; ++i) lds_copy(sv + i * kWaves * E::kPitch, rv, pl.dense[i]);
+  } else {
+    for (int i = 0; i < E::kBlocksPerWave; ++i) lds_copy(sk + i * kWaves * E::kPitch, rk, pl.tile[i]);
+    for (int i = 0; i < E::kBlocksPerWave; ++i) lds_copy(sv + i * kWaves * E::kPitch, rv, pl.tile[i]);
+  }
+}
+
 struct SoftmaxState {
   float M, L;
   float T;  // raw logit above which the reference max moves: (M + tau) / scale_log2
@@ -385,7 +572,7 @@ __device__ __forceinline__ void chunk_logits(const E& eng, const char* st, int l
 
 template <class E>
 __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_kernel(Params p) {
-  __shared__ __attribute__((aligned(16))) char smem[kStages * E::kStage];
+  __shared__ __attribute__((aligned(16))) char smem[E::kStages * E::kStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -464,7 +651,6 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
   const char* kbase = p.k + head_off;
   const char* vbase = p.v + head_off;
 
-  const DmaPlan<E> plan = make_plan<E>(wave, lane, p.gw);
   const MaskTable mt{(const_u64_t*)p.mask_tbl, p.mt_ky, p.mt_kx};
   const int mt_base = table_base(mt, sy0, sx0);
 
@@ -474,22 +660,32 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_fwd_ker
   const float inv_scale_log2 = 1.0f / p.scale_log2;
   SoftmaxState sm{kMInit, 0.0f, (kMInit + kLazyTau) * inv_scale_log2};
 
-  // ---- chunk walk (walk_chunks).  A chunk the wavefront's sub-tile does not
-  // touch contributes nothing to its rows: the wavefront skips its products
-  // and softmax and only takes part in the copies and barriers.
+  // ---- chunk walk.  A chunk the wavefront's sub-tile does not touch
+  // contributes nothing to its rows: the wavefront skips its products and
+  // softmax and only takes part in the copies and barriers.
   eng.settle_q();
-  walk_chunks(
-      ks, n_chunks, wave, smem, smem + E::kStage,
-      [&](char* st, const ChunkMeta& m, bool dense) { stage_chunk<E>(st, m, dense, wave, ks, kbase, vbase, plan); },
-      [&](const ChunkInfo& c, const char* st) {
-        if (!c.active) return;
-        typename E::Probs pr;
-        float alpha = 1.0f;
-        f32x16_t sc;
-        chunk_logits(eng, st, lane, sc, c, ks, qy, qx, p.r2, mt, mt_base);
-        if (chunk_softmax<E>(sm, sc, p.scale_log2, inv_scale_log2, pr, alpha)) eng.scale_o(alpha);
-        eng.pv(st, lane, pr);
-      });
+  auto compute = [&](const ChunkInfo& c, const char* st) {
+    if (!c.active) return;
+    typename E::Probs pr;
+    float alpha = 1.0f;
+    f32x16_t sc;
+    chunk_logits(eng, st, lane, sc, c, ks, qy, qx, p.r2, mt, mt_base);
+    if (chunk_softmax<E>(sm, sc, p.scale_log2, inv_scale_log2, pr, alpha)) eng.scale_o(alpha);
+    eng.pv(st, lane, pr);
+  };
+  if constexpr (__is_same(E, Bf16G)) {
+    const BlockPlan<E> plan = make_block_plan<E>(wave, lane, p.gw);
+    walk_chunks(
+        ks, n_chunks, wave, smem, smem + E::kStage,
+        [&](char* st, const ChunkMeta& m, bool dense) { stage_blocks<E>(st, m, dense, wave, kbase, vbase, plan); },
+        compute);
+  } else {
+    const DmaPlan<E> plan = make_plan<E>(wave, lane, p.gw);
+    walk_chunks(
+        ks, n_chunks, wave, smem, smem + E::kStage,
+        [&](char* st, const ChunkMeta& m, bool dense) { stage_chunk<E>(st, m, dense, wave, ks, kbase, vbase, plan); },
+        compute);
+  }
 
   // ---- epilogue
   const float Lt = sum_xor32(sm.L);
@@ -651,7 +847,7 @@ int attn_launch(const AttnLaunch& a, void* stream) {
 
   int rc;
   if (a.dtype == CLEAR_BF16) {
-    rc = a.d == 128 ? launch_main<Bf16<128>>(p, s, (int)grid) : launch_main<Bf16<64>>(p, s, (int)grid);
+    rc = a.d == 128 ? launch_main<Bf16G>(p, s, (int)grid) : launch_main<Bf16<64>>(p, s, (int)grid);
   } else {
     rc = a.d == 128 ? launch_main<F32<128>>(p, s, (int)grid) : launch_main<F32<64>>(p, s, (int)grid);
   }

@@ -85,7 +85,10 @@ def rocprof_command(kind: str, out_dir: str, cmd: List[str]) -> List[str]:
 
 def collect(out: str, cmd: List[str], passes: List[str], copy_cmd: Optional[List[str]],
             timeout_s: int) -> int:
-    """Run each pass as a child process.  Stops at the first failing pass."""
+    """Run each pass as a child process (from /tmp, where the profiler keeps its
+    scratch files; ``out`` is made absolute first).  Stops at the first failing
+    pass."""
+    out = os.path.abspath(out)
     os.makedirs(out, exist_ok=True)
     env = dict(os.environ)
     env.setdefault("TMPDIR", "/tmp")
@@ -119,8 +122,17 @@ def _rows(d: str, suffix: str):
 
 
 def _short(name: str) -> str:
-    """Kernel name without the argument list."""
-    return name.split("(")[0].strip()
+    """Kernel name without its final (argument list) group; demangled names
+    hold other parentheses, e.g. "(anonymous namespace)"."""
+    name = name.strip()
+    if not name.endswith(")"):
+        return name
+    depth = 0
+    for i in range(len(name) - 1, -1, -1):
+        depth += {")": 1, "(": -1}.get(name[i], 0)
+        if depth == 0:
+            return name[:i].strip()
+    return name
 
 
 def kernel_durations(d: str) -> Dict[str, List[float]]:

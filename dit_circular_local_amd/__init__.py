@@ -18,10 +18,10 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "ClearError", "fwd", "bwd", "fwd_strip", "text_merge", "strip_rows", "tile_map_size", "tile_map_build", "tile_map_build_device",
+    "ClearError", "fwd", "fwd_noalloc", "bwd", "fwd_strip", "text_merge", "strip_rows", "tile_map_size", "tile_map_build", "tile_map_build_device",
     "tile_map_descriptors", "release_cache", "last_error", "version", "lib", "EXPORTS",
     "CLEAR_OK", "CLEAR_EINVAL", "CLEAR_ENOMEM", "CLEAR_EHIP", "CLEAR_ENOTSUP",
-    "CLEAR_BF16", "CLEAR_FP32", "CLEAR_MERGE_EXACT", "CLEAR_MERGE_PATCH_AVERAGE", "CLEAR_WINDOW_CIRCLE", "CLEAR_WINDOW_SQUARE", "WINDOWS", "TILE_H", "TILE_W", "SUB_H", "SUB_W", "KEY_H", "KEY_W", "CHUNK",
+    "CLEAR_BF16", "CLEAR_FP32", "NOALLOC_SCRATCH_BYTES", "CLEAR_MERGE_EXACT", "CLEAR_MERGE_PATCH_AVERAGE", "CLEAR_WINDOW_CIRCLE", "CLEAR_WINDOW_SQUARE", "WINDOWS", "TILE_H", "TILE_W", "SUB_H", "SUB_W", "KEY_H", "KEY_W", "CHUNK",
     "MAX_GRID",
 ]
 
@@ -34,13 +34,14 @@ CLEAR_MERGE_EXACT, CLEAR_MERGE_PATCH_AVERAGE = 0, 1
 WINDOWS = {"circle": CLEAR_WINDOW_CIRCLE, "square": CLEAR_WINDOW_SQUARE}
 TILE_H, TILE_W, SUB_H, SUB_W, KEY_H, KEY_W, CHUNK = 16, 8, 4, 8, 4, 8, 32
 MAX_GRID = 8192
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # every entry point declared in include/clear_attn.h
 EXPORTS = (
     "clear_attn_fwd", "clear_attn_fwd_ex", "clear_tile_map_size", "clear_tile_map_build",
     "clear_tile_map_build_device", "clear_tile_map_size_ex", "clear_tile_map_build_ex",
     "clear_tile_map_build_device_ex", "clear_attn_fwd_strip", "clear_text_merge", "clear_attn_bwd",
-    "clear_tile_map_descriptors", "clear_last_error",
+    "clear_tile_map_descriptors", "clear_attn_fwd_noalloc", "clear_last_error",
     "clear_release_cache", "clear_version",
 )
 
@@ -85,6 +86,8 @@ def lib():
     L.clear_tile_map_build_ex.restype = i
     L.clear_tile_map_build_device_ex.argtypes = [i] + L.clear_tile_map_build_device.argtypes
     L.clear_tile_map_build_device_ex.restype = i
+    L.clear_attn_fwd_noalloc.argtypes = [p, p, p, p, i, i, i, i, i, i, ctypes.POINTER(_Opts), p]
+    L.clear_attn_fwd_noalloc.restype = i
     L.clear_tile_map_descriptors.argtypes = [i, i, i, i, p, p, p, p, sz, szp, p]
     L.clear_tile_map_descriptors.restype = i
     L.clear_attn_fwd_strip.argtypes = [p, p, p, p, i, i, i, i, i, i, ctypes.POINTER(_Opts), i, i, i, p, p, p]
@@ -191,6 +194,38 @@ def fwd(q, k, v, n_text: int, grid_h: int, grid_w: int, radius: Optional[int] = 
                                  B, H, d, n_text, grid_h, grid_w, ctypes.byref(opts), stream)
     _check(rc)
     return (out, lse) if return_lse else out
+
+
+def fwd_noalloc(q, k, v, n_text: int, grid_h: int, grid_w: int, radius: Optional[int] = None,
+                r2: Optional[int] = None, out=None, lse=None, text_splits: int = 0, window: str = "circle"):
+    """The forward through clear_attn_fwd_noalloc: the library allocates nothing
+    (its tile map and text-row partials live in a fixed per-GPU scratch; see
+    include/clear_attn.h).  ``out`` (and ``lse`` [B, H, N] float32, if wanted)
+    are the caller's; when ``out`` is None it is allocated here by torch,
+    before the call.  Returns ``out``."""
+    import torch
+
+    dtype = _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    if N != n_text + grid_h * grid_w:
+        raise ValueError(f"N = {N} != n_text + grid_h * grid_w = {n_text + grid_h * grid_w}")
+    if (radius is None) == (r2 is None):
+        raise ValueError("give exactly one of radius and r2")
+    if r2 is None:
+        if radius < 0:
+            raise ValueError("radius must be >= 0")
+        r2 = min(int(radius) * int(radius), 2 ** 31 - 1)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _expect(out, "out", q.device, q.dtype, q.shape)
+    if lse is not None:
+        _expect(lse, "lse", q.device, torch.float32, (B, H, N))
+    opts = _Opts(dtype, int(r2), lse.data_ptr() if lse is not None else None, int(text_splits),
+                 _window_code(window))
+    _check(lib().clear_attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, d,
+                                        n_text, grid_h, grid_w, ctypes.byref(opts), _stream_of(q)))
+    return out
 
 
 def _check_qkv(q, k, v):

@@ -131,37 +131,6 @@ int get_tile_map(DevState& ds, int gh, int gw, int r2, int window, hipStream_t s
   return CLEAR_OK;
 }
 
-// Text-row split count: make a text workgroup's key range (its critical path)
-// at most about half of the ideal time of the whole launch.  With fill_slots
-// (the forward), also at least enough splits for the text workgroups to take
-// one workgroup slot each across the chip: on the 512x512 + 512 FLUX shape
-// (24 heads) that is 8 splits, measured 1.5-3 % faster than the 2 (r = 32) and
-// 5 (r = 8) of the critical-path rule alone, and neutral on 256x256 + 512.
-int choose_text_splits(int B, int H, int n_text, int N, int ntiles, size_t img_chunks, int n_cu,
-                       double waves_per_simd = 3.0, bool fill_slots = false) {
-  // img_chunks: listed key tiles (32 keys each) over all query tiles
-  if (n_text == 0) return 1;
-  const double nall = (N + CLEAR_CHUNK - 1) / CLEAR_CHUNK;
-  const double text_blocks = (n_text + 127) / 128;
-  const double nt_ch = (n_text + CLEAR_CHUNK - 1) / CLEAR_CHUNK;
-  // wavefront-chunks of work (each = 32 queries x 32 keys)
-  const double w_img = (double)B * H * (4.0 * ntiles * nt_ch + 3.0 * (double)img_chunks);
-  const double w_text = (double)B * H * text_blocks * 4.0 * nall;
-  const double slots = (double)n_cu * 4.0 * waves_per_simd;  // CUs x SIMDs x resident waves
-  const double t_ideal = (w_img + w_text) / slots;
-  int s = (int)(2.0 * nall / (t_ideal > 1.0 ? t_ideal : 1.0)) + 1;
-  if (fill_slots) {
-    const double wg_slots = (double)n_cu * waves_per_simd;  // workgroups of 4 wavefronts resident on the device
-    const int s_fill = (int)(wg_slots / ((double)B * H * text_blocks));
-    if (s_fill > s) s = s_fill;
-  }
-  int smax = (int)(nall / 8.0);
-  if (s > smax) s = smax;
-  if (s > 64) s = 64;
-  if (s < 1) s = 1;
-  return s;
-}
-
 // The device's library workspace, grown to at least `need` bytes, for kernels
 // about to be enqueued on stream s.  If the previous user ran on another
 // stream, s first waits (on the device) for that user's kernels, so calls on
@@ -208,6 +177,37 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 }  // namespace
 
+// Text-row split count: make a text workgroup's key range (its critical path)
+// at most about half of the ideal time of the whole launch.  With fill_slots
+// (the forward), also at least enough splits for the text workgroups to take
+// one workgroup slot each across the chip: on the 512x512 + 512 FLUX shape
+// (24 heads) that is 8 splits, measured 1.5-3 % faster than the 2 (r = 32) and
+// 5 (r = 8) of the critical-path rule alone, and neutral on 256x256 + 512.
+int choose_text_splits(int B, int H, int n_text, int N, int ntiles, size_t img_chunks, int n_cu,
+                       double waves_per_simd, bool fill_slots) {
+  // img_chunks: listed key tiles (32 keys each) over all query tiles
+  if (n_text == 0) return 1;
+  const double nall = (N + CLEAR_CHUNK - 1) / CLEAR_CHUNK;
+  const double text_blocks = (n_text + 127) / 128;
+  const double nt_ch = (n_text + CLEAR_CHUNK - 1) / CLEAR_CHUNK;
+  // wavefront-chunks of work (each = 32 queries x 32 keys)
+  const double w_img = (double)B * H * (4.0 * ntiles * nt_ch + 3.0 * (double)img_chunks);
+  const double w_text = (double)B * H * text_blocks * 4.0 * nall;
+  const double slots = (double)n_cu * 4.0 * waves_per_simd;  // CUs x SIMDs x resident waves
+  const double t_ideal = (w_img + w_text) / slots;
+  int s = (int)(2.0 * nall / (t_ideal > 1.0 ? t_ideal : 1.0)) + 1;
+  if (fill_slots) {
+    const double wg_slots = (double)n_cu * waves_per_simd;  // workgroups of 4 wavefronts resident on the device
+    const int s_fill = (int)(wg_slots / ((double)B * H * text_blocks));
+    if (s_fill > s) s = s_fill;
+  }
+  int smax = (int)(nall / 8.0);
+  if (s > smax) s = smax;
+  if (s > 64) s = 64;
+  if (s < 1) s = 1;
+  return s;
+}
+
 int set_error(int code, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -233,7 +233,7 @@ using namespace clear;
 
 extern "C" const char* clear_last_error(void) { return g_err; }
 
-extern "C" int clear_version(void) { return 10400; }
+extern "C" int clear_version(void) { return 10500; }
 
 namespace {
 
@@ -246,9 +246,12 @@ struct StripArgs {
   float* part_ml;
 };
 
-int run_forward(const void* q, const void* k, const void* v, void* out, int B, int H, int d,
-                int n_text, int grid_h, int grid_w, const clear_opts* opts, const StripArgs* strip,
-                void* stream) {
+}  // namespace
+
+// Argument checks of the forward entry points (see clear_attn.h); *o receives
+// the options with their defaults filled in.
+int validate_forward(const void* q, const void* k, const void* v, void* out, int B, int H, int d, int n_text,
+                     int grid_h, int grid_w, const clear_opts* opts, const StripArgs* strip, clear_opts* o_out) {
   clear_opts o = opts ? *opts : clear_opts{CLEAR_BF16, 0, nullptr, 0, CLEAR_WINDOW_CIRCLE};
   if (!q || !k || !v || !out) return set_error(CLEAR_EINVAL, "q, k, v and out must not be NULL");
   if (B < 1 || H < 1) return set_error(CLEAR_EINVAL, "B and H must be >= 1 (got %d, %d)", B, H);
@@ -287,6 +290,19 @@ int run_forward(const void* q, const void* k, const void* v, void* out, int B, i
     return set_error(CLEAR_EINVAL, "out must not overlap q, k or v");
   if (o.lse_out && ((uintptr_t)o.lse_out & 3)) return set_error(CLEAR_EINVAL, "lse_out must be 4-byte aligned");
 
+  *o_out = o;
+  return CLEAR_OK;
+}
+
+namespace {
+
+int run_forward(const void* q, const void* k, const void* v, void* out, int B, int H, int d,
+                int n_text, int grid_h, int grid_w, const clear_opts* opts, const StripArgs* strip,
+                void* stream) {
+  clear_opts o;
+  int rc0 = validate_forward(q, k, v, out, B, H, d, n_text, grid_h, grid_w, opts, strip, &o);
+  if (rc0) return rc0;
+  const long long N = (long long)n_text + (long long)grid_h * grid_w;
   hipStream_t s = (hipStream_t)stream;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -448,6 +464,89 @@ extern "C" int clear_attn_fwd_ex(const void* q, const void* k, const void* v, vo
                                  const clear_opts* opts, void* stream) {
   clear_error_reset();
   return run_forward(q, k, v, out, B, H, d, n_text, grid_h, grid_w, opts, nullptr, stream);
+}
+
+extern "C" int clear_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, int B, int H,
+                                      int d, int n_text, int grid_h, int grid_w, const clear_opts* opts,
+                                      void* stream) {
+  clear_error_reset();
+  clear_opts o;
+  int rc = validate_forward(q, k, v, out, B, H, d, n_text, grid_h, grid_w, opts, nullptr, &o);
+  if (rc) return rc;
+  const long long N = (long long)n_text + (long long)grid_h * grid_w;
+  const size_t cap = CLEAR_NOALLOC_SCRATCH_BYTES;
+
+  // the tile map at the kernels' tiling, laid out as the cached copy (sized on
+  // the host before any HIP call)
+  TileGeom g = make_geom(grid_h, grid_w, o.r2_max, CLEAR_TILE_H, CLEAR_TILE_W, CLEAR_SUB_H, CLEAR_SUB_W,
+                         CLEAR_KEY_H, CLEAR_KEY_W, o.window);
+  const size_t n_entries = tile_map_count(g);
+  if (n_entries > (size_t)kMaxKernelEntries)
+    return set_error(CLEAR_ENOTSUP, "the tile map holds %zu key tiles; the attention kernels index at most %d",
+                     n_entries, kMaxKernelEntries);
+  const size_t nt = (size_t)g.nty * g.ntx;
+  const size_t o_kt = align_up((nt + 1) * 4, 256);
+  const size_t o_fl = align_up(o_kt + n_entries * 4, 256);
+  const size_t o_ds = align_up(o_fl + n_entries * 2 + 2, 256);
+  const size_t map_bytes = align_up(o_ds + n_entries * 16, 256);
+  if (map_bytes > cap)
+    return set_error(CLEAR_ENOMEM, "the tile map of a %d x %d grid at r2 %d needs %zu bytes; the no-alloc "
+                     "scratch holds %zu", grid_h, grid_w, g.r2, map_bytes, cap);
+
+  if (o.text_splits > 1 && n_text > 0 &&
+      (size_t)o.text_splits * (align_up((size_t)B * H * n_text * d * 4, 256) +
+                               align_up((size_t)B * H * n_text * 8, 256)) > cap - map_bytes)
+    return set_error(CLEAR_ENOMEM, "%d text splits do not fit the no-alloc scratch beside the tile map",
+                     o.text_splits);
+
+  hipStream_t s = (hipStream_t)stream;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  int n_cu = 0;
+  if ((e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+    return hip_fail(e, "hipDeviceGetAttribute");
+  void* base = nullptr;
+  if ((rc = noalloc_scratch(dev, &base)) != CLEAR_OK) return rc;
+
+  // text-row partials beside it
+  const size_t per_split = align_up((size_t)B * H * n_text * d * 4, 256) + align_up((size_t)B * H * n_text * 8, 256);
+  const size_t room = (cap - map_bytes) / (per_split ? per_split : 1);
+  int splits = o.text_splits ? o.text_splits
+                             : choose_text_splits(B, H, n_text, (int)N, (int)nt, n_entries, n_cu > 0 ? n_cu : 256,
+                                                  3.0, true);
+  if (n_text > 0 && splits > 1 && (size_t)splits > room) {
+    if (o.text_splits)
+      return set_error(CLEAR_ENOMEM, "%d text splits need %zu bytes of partials; the no-alloc scratch has %zu "
+                       "left beside the tile map", splits, (size_t)splits * per_split, cap - map_bytes);
+    splits = room > 1 ? (int)room : 1;
+  }
+
+  char* b = (char*)base;
+  AttnLaunch a;
+  memset(&a, 0, sizeof a);
+  a.q = q; a.k = k; a.v = v; a.out = out; a.lse = o.lse_out;
+  a.tm_offsets = (const uint32_t*)b;
+  a.tm_desc = (const uint32_t*)(b + o_ds);
+  a.mask_tbl = nullptr;
+  a.B = B; a.H = H; a.d = d; a.n_text = n_text; a.gh = grid_h; a.gw = grid_w; a.r2 = g.r2;
+  a.dtype = o.dtype; a.text_splits = splits; a.window = o.window;
+  a.row_begin = 0;
+  a.row_end = grid_h;
+  if (splits > 1 && n_text > 0) {
+    a.ws_o = (float*)(b + map_bytes);
+    a.ws_ml = (float*)(b + map_bytes + (size_t)splits * align_up((size_t)B * H * n_text * d * 4, 256));
+  }
+  rc = tile_map_build_device_launch(g, (uint32_t*)b, (uint32_t*)(b + o_kt), (uint16_t*)(b + o_fl),
+                                    (uint32_t*)(b + o_ds), stream);
+  if (rc) return rc;
+  rc = attn_launch(a, stream);
+  if (rc) return rc;
+  if (debug_sync_enabled()) {
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "CLEAR_DEBUG sync");
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "CLEAR_DEBUG check");
+  }
+  return CLEAR_OK;
 }
 
 extern "C" int clear_attn_fwd_strip(const void* q, const void* k, const void* v, void* out, int B,

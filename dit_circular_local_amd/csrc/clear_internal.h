@@ -75,6 +75,15 @@ struct AttnLaunch {
 
 int attn_launch(const AttnLaunch& a, void* stream);
 
+// Text-row split count of the layer entry points (clear_attn.cpp).
+int choose_text_splits(int B, int H, int n_text, int N, int ntiles, size_t img_chunks, int n_cu,
+                       double waves_per_simd = 3.0, bool fill_slots = false);
+
+// Device address of the allocation-free entry point's scratch on device dev
+// (noalloc.hip): CLEAR_NOALLOC_SCRATCH_BYTES bytes, looked up on the first call
+// for the device, which must be current.
+int noalloc_scratch(int dev, void** ptr);
+
 // Backward launch description (all pointers are device pointers).
 struct BwdLaunch {
   const void* q;

@@ -321,6 +321,37 @@ int clear_tile_map_descriptors(int window, int grid_h, int grid_w, int r2_max,
                                uint32_t* offsets, uint32_t* key_tiles, uint16_t* flags,
                                uint32_t* desc, size_t cap, size_t* n_entries, void* stream);
 
+/* Size of the fixed device scratch of clear_attn_fwd_noalloc (64 MiB per GPU). */
+#define CLEAR_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * clear_attn_fwd_noalloc -- clear_attn_fwd_ex without any allocation, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc (added in 1.5).
+ *
+ * Same arguments, checks, result and errors as clear_attn_fwd_ex (the caller
+ * still passes q, k, v, out and the optional lse_out).  Instead of the
+ * library's cached tile map and workspace, it uses one fixed device array of
+ * CLEAR_NOALLOC_SCRATCH_BYTES per GPU, which the device holds from this
+ * entry point's first call on it (when its address is looked up, with that
+ * device current) until the process ends.  Every call rebuilds the tile map
+ * there on `stream` (three small kernels) and keeps the text-row partials
+ * there; it computes the window mask per element (no lane-mask table).  It
+ * calls no hipMalloc, hipFree, hipMallocAsync or other allocating routine, and
+ * creates no events.
+ * Limits: the tile map must fit the scratch, else CLEAR_ENOMEM and nothing is
+ * launched (the 512 x 512 grid at radius 32 takes 6.9 MB); the text rows use
+ * the library's split count, lowered until the partials fit beside the map
+ * (one split needs none); an explicit opts->text_splits whose partials do not
+ * fit returns CLEAR_ENOMEM.
+ * All calls on one GPU share its scratch, which keeps the last call's
+ * contents: calls that overlap on one GPU (other streams, other host threads
+ * without ordering) race on it and must be serialised by the caller.
+ */
+int clear_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out,
+                           int B, int H, int d, int n_text, int grid_h, int grid_w,
+                           const clear_opts* opts, void* stream);
+
 /* Message of the last error raised on the calling thread ("" if none). */
 const char* clear_last_error(void);
 

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert ca.version() == 10400  # 1.4.0: tile-map descriptors exported (clear_tile_map_descriptors)
+    assert ca.version() == 10500  # 1.5.0: allocation-free forward (clear_attn_fwd_noalloc)
 
 
 # fake, aligned, non-overlapping device addresses: validation must fail before use
@@ -244,3 +244,27 @@ def test_descriptor_builder_checks_before_launch():
     assert L.clear_tile_map_descriptors(0, 64, 64, 64, 0x1000, 0x2000, 0x3000, None, n.value,
                                         ctypes.byref(n), None) == ca.CLEAR_EINVAL
     assert "NULL" in ca.last_error()
+
+
+def _noalloc(splits=0, q=Q, k=K, v=V, o=O, **kw):
+    a = dict(ok)
+    a.update(kw)
+    opts = ca._Opts(0, a.pop("r2", 4), None, splits, 0)
+    return ca.lib().clear_attn_fwd_noalloc(q, k, v, o, a["B"], a["H"], a["d"], a["n_text"], a["gh"], a["gw"],
+                                           ctypes.byref(opts), None)
+
+
+def test_noalloc_forward_checks_before_any_hip_call():
+    """The allocation-free forward shares the forward's argument checks, and
+    refuses, before touching the device, a tile map that does not fit its fixed
+    scratch (a 4096 x 4096 grid at r = 32 needs some 440 MB) and explicit text
+    splits whose partials do not fit beside the map."""
+    for kw, frag in [(dict(d=96), "d must be"), (dict(q=0), "NULL"), (dict(o=Q + 16), "overlap"),
+                     (dict(gh=0), "grid sides")]:
+        assert _noalloc(**kw) == ca.CLEAR_EINVAL
+        assert frag in ca.last_error()
+    big = 0x4000000000  # far apart: 4096^2 tokens of d 128 bf16 are 4.3 GB per tensor
+    rc = _noalloc(q=big, k=2 * big, v=3 * big, o=4 * big, B=1, H=1, n_text=512, gh=4096, gw=4096, r2=1024)
+    assert rc == ca.CLEAR_ENOMEM and "no-alloc scratch" in ca.last_error()
+    rc = _noalloc(splits=64, B=1, H=24, n_text=512, gh=64, gw=64, r2=256)
+    assert rc == ca.CLEAR_ENOMEM and "text splits" in ca.last_error()

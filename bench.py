@@ -18,7 +18,6 @@ Prints ONE JSON line on stdout (progress goes to stderr).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -82,38 +81,12 @@ def computed_pairs(ca, n_text: int, gh: int, gw: int, r2: int, window: str = "ci
     return (dense + touched + text_rows) * per_chunk
 
 
-# sources the forward attention kernel is compiled and launched from (launch
-# configuration included); with the device code-generation flags they key its
-# traffic figures, which hold only while both are unchanged
-FWD_KERNEL_SOURCES = ("dit_circular_local_amd/csrc/attn_fwd.hip", "dit_circular_local_amd/csrc/attn_common.h",
-                      "dit_circular_local_amd/csrc/clear_internal.h", "dit_circular_local_amd/csrc/tile_geom.h",
-                      "include/clear_attn.h", "dit_circular_local_amd/csrc/clear_attn.cpp")
+def load_profile(workload: str, radius: int):
+    """Figures of the forward kernel from the committed rocprofv3 runs
+    (profiles/traffic.json, written by dit_circular_local_amd.profiling), if they
+    were taken on the current kernel sources and device flags (else None)."""
+    from dit_circular_local_amd.build import kernel_source_hash
 
-
-def _code_only(text: str) -> str:
-    """Source text without comments and with whitespace collapsed: edits to
-    comments leave the hash (and the compiled kernel) unchanged."""
-    import re
-
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    return " ".join(text.split())
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for name in FWD_KERNEL_SOURCES:
-        with open(os.path.join(ROOT, name), encoding="utf-8") as f:
-            h.update(name.encode() + _code_only(f.read()).encode())
-    from dit_circular_local_amd.build import DEVICE_FLAGS
-
-    h.update(" ".join(DEVICE_FLAGS).encode())
-    return h.hexdigest()[:16]
-
-
-def load_traffic(workload: str, radius: int):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources and device flags (else None)."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
@@ -122,7 +95,7 @@ def load_traffic(workload: str, radius: int):
     e = t.get(f"{workload}_r{radius}")
     if not e or e.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return e.get("hbm_bytes_per_launch")
+    return e
 
 
 def time_layer(ca, torch, q, k, v, w, radius, steps, warmup, window="circle"):
@@ -251,46 +224,105 @@ def time_backward(ca, torch, q, k, v, w, radius, steps, warmup):
     return ms[len(ms) // 2], sum(ms) / len(ms)
 
 
-def cpu_baseline(q, k, v, w, radius, budget_s):
-    """The fp64 oracle, untuned, on a bounded sample of the same layer: head 0,
-    its first 64 text rows, then 8x8 image blocks spread over the grid until the
-    time budget is spent.  Reported in the metric's unit (in-window TFLOP/s)."""
-    import numpy as np
+def _oracle_worker(args):
+    """One worker of the CPU baseline: regenerates its head of the workload from
+    the seeded generator, waits for the others, then runs the fp64 oracle on
+    text rows and whole rows of 8x8 image blocks until its time budget is spent.
+    Returns (admitted pairs, text rows, block rows, seconds of oracle work)."""
+    (wname, seed, head, radius, budget_s, first_block_row, barrier) = args
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+    from dit_circular_local_amd.inputs import WORKLOADS, make_head
     from oracle import attention_head, in_window_pairs
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
-    qh = q[0, 0].float().cpu().numpy()
-    kh = k[0, 0].float().cpu().numpy()
-    vh = v[0, 0].float().cpu().numpy()
+    w = WORKLOADS[wname]
+    qh, kh, vh = (make_head(w.n, w.d, t, 0, head, seed, w.dtype, w.rms_norm, w.scale).float().numpy()
+                  for t in ("q", "k", "v"))
     r2 = radius * radius
     nby, nbx = -(-w.grid_h // 8), -(-w.grid_w // 8)
-    order = np.random.default_rng(0).permutation(nby * nbx)
-    text_rows = list(range(min(64, w.n_text)))
+    text_rows = list(range((16 * head) % w.n_text, (16 * head) % w.n_text + 16)) if w.n_text >= 16 else []
+    barrier.wait()
     t0 = time.perf_counter()
     attention_head(qh, kh, vh, w.n_text, w.grid_h, w.grid_w, r2, text_rows=text_rows, blocks=[])
-    done = []
-    i = 0
-    while time.perf_counter() - t0 < budget_s and i < len(order):
-        batch = [(int(b) // nbx, int(b) % nbx) for b in order[i:i + 16]]
-        attention_head(qh, kh, vh, w.n_text, w.grid_h, w.grid_w, r2, text_rows=[], blocks=batch)
-        done += batch
-        i += 16
+    blocks, rows_done = [], 0
+    while time.perf_counter() - t0 < budget_s and rows_done < nby:
+        by = (first_block_row + rows_done) % nby
+        row = [(by, bx) for bx in range(nbx)]
+        attention_head(qh, kh, vh, w.n_text, w.grid_h, w.grid_w, r2, text_rows=[], blocks=row)
+        blocks += row
+        rows_done += 1
     secs = time.perf_counter() - t0
-    pairs = in_window_pairs(w.n_text, w.grid_h, w.grid_w, r2, text_rows=text_rows, blocks=done)
+    pairs = in_window_pairs(w.n_text, w.grid_h, w.grid_w, r2, text_rows=text_rows, blocks=blocks)
+    return pairs, len(text_rows), rows_done, secs
+
+
+def cpu_baseline(w, radius, budget_s, seed=0):
+    """The fp64 oracle, untuned, on a bounded sample of the same layer, over a
+    process pool on the host's cores (one BLAS thread per worker): worker i
+    takes head i (mod H), 16 of its text rows and whole rows of 8x8 image
+    blocks (spread over the grid) until `budget_s` seconds of oracle work are
+    spent.  Reported in the metric's unit: 4 d x admitted pairs / the slowest
+    worker's seconds (the workers run at once), with the full layer's time at
+    that rate as an extrapolation."""
+    import multiprocessing as mp
+
+    ncpu = os.cpu_count() or 1
+    workers = max(1, min(ncpu, 16))
+    nby = -(-w.grid_h // 8)
+    ctx = mp.get_context("spawn")  # the parent holds a GPU context: never fork it
+    with ctx.Manager() as mgr:
+        barrier = mgr.Barrier(workers)
+        jobs = [(w.name, seed, i % w.H, radius, budget_s, (i * nby) // workers, barrier) for i in range(workers)]
+        with ctx.Pool(workers) as pool:
+            res = pool.map(_oracle_worker, jobs)
+    pairs = sum(r[0] for r in res)
+    secs = max(r[3] for r in res)
     tflops = 4.0 * w.d * pairs / secs / 1e12
+    layer_flops = 4.0 * w.d * admitted_pairs(w.n_text, w.grid_h, w.grid_w, radius * radius) * w.B * w.H
     return {
         "value": tflops,
         "unit": "TFLOP/s",
-        "cores": threads,
+        "cores": workers,
         "kind": "oracle",
-        "sample": f"head 0 of 24: {len(text_rows)} text rows + {len(done)} of {nby * nbx} 8x8 image "
-                  f"blocks (r={radius}), {pairs} admitted pairs in {secs:.1f} s, fp64 numpy",
+        "sample": f"{workers} worker processes, one per head {sorted(set(j % w.H for j in range(workers)))}: "
+                  f"16 text rows and whole rows of 8x8 image blocks each ({sum(r[2] for r in res)} block rows "
+                  f"of {nby}) for ~{budget_s:.0f} s, r={radius}; {pairs} admitted pairs in {secs:.1f} s; fp64 numpy",
         "seconds": secs,
+        "os_cpu_count": ncpu,
+        "worker_processes": workers,
+        "blas_threads_per_worker": 1,
+        "radius": radius,
+        "full_layer_seconds_extrapolated": layer_flops / (tflops * 1e12),
     }
+
+
+def time_configs(ca, torch, steps=5, warmup=2):
+    """Every workload configuration the parity tests cover (tiny fp32, and the
+    1024^2 .. 8192^2 FLUX shapes at each of their radii): ms per layer (median
+    of `steps` calls, HIP events) and in-window TFLOP/s."""
+    from dit_circular_local_amd.inputs import WORKLOADS, workload_qkv
+
+    out = {}
+    for name in ("tiny", "flux1k", "flux2k", "flux4k", "flux8k"):
+        w = WORKLOADS[name]
+        q, k, v = workload_qkv(w, seed=0, device="cuda")
+        for r in w.radii:
+            t, _ = time_layer(ca, torch, q, k, v, w, r, steps, warmup)
+            flops = 4.0 * w.d * admitted_pairs(w.n_text, w.grid_h, w.grid_w, r * r) * w.B * w.H
+            out[f"{name}_r{r}"] = {
+                "ms_per_layer": round(t["kernel_ms_median"], 4),
+                "in_window_tflops": round(flops / (t["kernel_ms_median"] * 1e-3) / 1e12, 3),
+                "pct_bf16_peak": round(100.0 * flops / (t["kernel_ms_median"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)
+                if w.dtype == "bf16" else None,
+                "dtype": w.dtype,
+            }
+            log(f"config {name} r={r}: {t['kernel_ms_median']:.4f} ms, {out[f'{name}_r{r}']['in_window_tflops']} TFLOP/s")
+        del q, k, v
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -307,7 +339,9 @@ def main():
                     help="also time the layer as this many horizontal strips plus text merges (0: none)")
     ap.add_argument("--backward-radii", default="32,8",
                     help="also time the backward (clear_attn_bwd) at these radii ('' : none)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="oracle work per worker and radius for the CPU baseline")
+    ap.add_argument("--no-configs", action="store_true", help="skip timing the other workload configurations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times) and exit: "
@@ -379,7 +413,8 @@ def main():
     main_r = args.radius
     m = results[main_r]
     achieved = m["flops_per_layer"] / (m["kernel_ms_mean"] * 1e-3) / 1e12
-    traffic = load_traffic(w.name, main_r)
+    prof = load_profile(w.name, main_r)
+    traffic = prof.get("hbm_bytes_per_launch") if prof else None
     line = {
         "metric": "in-window attention TFLOP/s (CLEAR forward, 8192x8192, r=32; ms/layer and r=8 alongside)",
         "value": round(m["in_window_tflops"], 3),
@@ -411,7 +446,13 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "clear_attn_fwd_kernel<Bf16<128>> + clear_text_merge_kernel (HIP events around each call)",
+            "kernel": "clear_attn_fwd_kernel<Bf16G> + clear_text_merge_kernel (HIP events around each call)",
+            # from the committed counter runs of these sources (null when they changed since):
+            # matrix-core busy share of SIMD cycles, and the fabric bytes above per this run's
+            # mean launch time
+            "mfma_util": round(prof["mfma_busy"], 4) if prof and prof.get("mfma_busy") else None,
+            "hbm_gbps": round(traffic / (m["kernel_ms_mean"] * 1e-3) / 1e9, 1) if traffic else None,
+            "profile_kernel_ms": round(prof["kernel_ms"], 4) if prof and prof.get("kernel_ms") else None,
         },
     }
     # the pages' figures, context only (another machine, and end-to-end numbers
@@ -457,9 +498,16 @@ def main():
             "flops_per_layer": bflops,
         }
         log(f"backward r={r}: {med:.3f} ms/layer, {line[f'backward_r{r}']['in_window_tflops']:.1f} TFLOP/s in-window")
+    if not args.no_configs:
+        line["configs"] = time_configs(ca, torch)
     if not args.no_cpu_baseline:
-        log(f"timing the CPU oracle on a sample (~{args.cpu_seconds:.0f} s)...")
-        line["cpu_baseline"] = cpu_baseline(q, k, v, w, main_r, args.cpu_seconds)
+        del q, k, v
+        torch.cuda.empty_cache()
+        for r in radii:
+            log(f"timing the CPU oracle on a sample, r={r} (~{args.cpu_seconds:.0f} s per worker)...")
+            cb = cpu_baseline(w, r, args.cpu_seconds)
+            line["cpu_baseline" if r == main_r else f"cpu_baseline_r{r}"] = cb
+            log(f"CPU oracle r={r}: {cb['value']:.4f} TFLOP/s on {cb['worker_processes']} processes")
     print(json.dumps(line), flush=True)
 
 

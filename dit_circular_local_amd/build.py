@@ -28,6 +28,37 @@ DEVICE_FLAGS = [
 ]
 
 
+# sources the forward attention kernel is compiled and launched from (launch
+# configuration included); with the device code-generation flags they key the
+# committed profile figures, which hold only while both are unchanged
+FWD_KERNEL_SOURCES = ("dit_circular_local_amd/csrc/attn_fwd.hip", "dit_circular_local_amd/csrc/attn_common.h",
+                      "dit_circular_local_amd/csrc/clear_internal.h", "dit_circular_local_amd/csrc/tile_geom.h",
+                      "include/clear_attn.h", "dit_circular_local_amd/csrc/clear_attn.cpp")
+
+
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace collapsed: edits to
+    comments leave the hash (and the compiled kernel) unchanged."""
+    import re
+
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_source_hash() -> str:
+    """16 hex digits of SHA-256 over the forward kernel's sources (code only)
+    and the device flags."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in FWD_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, name), encoding="utf-8") as f:
+            h.update(name.encode() + _code_only(f.read()).encode())
+    h.update(" ".join(DEVICE_FLAGS).encode())
+    return h.hexdigest()[:16]
+
+
 def build_command(out: str = LIB):
     return [
         HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

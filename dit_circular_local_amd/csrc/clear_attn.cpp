@@ -1,6 +1,6 @@
 // clear_attn.cpp -- C ABI of libclear_attn.so: argument checks, tile-map cache,
 // text-row workspace and launch sequencing.  See include/clear_attn.h.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <cstdarg>
 #include <cstdio>

@@ -299,6 +299,9 @@ def main(argv=None) -> int:
     s.add_argument("--md", default=None)
     s.add_argument("--json", default=None)
     s.add_argument("--title", default="rocprofv3 summary")
+    s.add_argument("--record", default=None, help="JSON file to add this run's figures to (profiles/traffic.json)")
+    s.add_argument("--key", default=None, help="entry name in --record, e.g. flux8k_r32")
+    s.add_argument("--source", default=None, help="name of the Markdown summary the entry refers to")
     a = ap.parse_args(argv)
     if a.cmd == "collect":
         cmd = a.command[1:] if a.command and a.command[0] == "--" else a.command
@@ -321,7 +324,40 @@ def main(argv=None) -> int:
     if a.json:
         with open(a.json, "w") as f:
             json.dump(res, f, indent=1)
+    if a.record:
+        record(a.record, a.key, res, a.source)
     return 0
+
+
+def record(path: str, key: str, res: dict, source: Optional[str]) -> None:
+    """Add the figures bench.py reads (keyed by the forward kernel's source
+    hash) to a JSON file, as entry `key`."""
+    from dit_circular_local_amd.build import kernel_source_hash
+
+    d = res["derived"]
+    entry = {
+        "kernel_source_hash": kernel_source_hash(),
+        "kernel": res["kernel"],
+        "kernel_ms": res.get("trace", {}).get("mean_ms"),
+        "hbm_bytes_per_launch": d.get("bytes"),
+        "read_bytes": d.get("read_bytes"),
+        "write_bytes": d.get("write_bytes"),
+        "fetch_scale": d.get("fetch_scale"),
+        "write_scale": d.get("write_scale"),
+        "mfma_busy": d.get("mfma_busy"),
+        "valu_active": d.get("valu_active"),
+        "valu_mfma_coexec": d.get("valu_mfma_coexec"),
+        "shader_clock_ghz": d.get("shader_clock_ghz"),
+        "source": source,
+    }
+    data = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            data = json.load(f)
+    data[key] = entry
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1)
+        f.write("\n")
 
 
 if __name__ == "__main__":

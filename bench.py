@@ -239,7 +239,9 @@ def _oracle_worker(args):
     from oracle import attention_head, in_window_pairs
 
     w = WORKLOADS[wname]
-    qh, kh, vh = (make_head(w.n, w.d, t, 0, head, seed, w.dtype, w.rms_norm, w.scale).float().numpy()
+    # widened to float64 here, outside the timed region (the oracle would otherwise
+    # widen the whole head again on every call)
+    qh, kh, vh = (make_head(w.n, w.d, t, 0, head, seed, w.dtype, w.rms_norm, w.scale).double().numpy()
                   for t in ("q", "k", "v"))
     r2 = radius * radius
     nby, nbx = -(-w.grid_h // 8), -(-w.grid_w // 8)

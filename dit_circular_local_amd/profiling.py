@@ -246,13 +246,23 @@ def _copy_kib(root: str) -> Optional[float]:
     return None
 
 
-def markdown(res: dict, title: str) -> str:
+def _repo_relative(cmd: str) -> str:
+    """A recorded command with the checkout's absolute path written as $REPO."""
+    import re
+
+    return re.sub(r"/\S*?/repo(?=/)", "$REPO", cmd)
+
+
+def markdown(res: dict, title: str, note: Optional[str] = None) -> str:
     """A short Markdown summary of ``summarize``'s record."""
     lines = [f"# {title}", ""]
+    if note:
+        lines += [note, ""]
+    lines += ["Commands (each pass its own profiler run, from /tmp; `$REPO` is the repository root):", ""]
     for p in ("trace", "sq", "sq2", "fetch", "write", "copy_fetch", "copy_write"):
         cmdf = os.path.join(res["root"], f"{p}.cmd")
         if os.path.exists(cmdf):
-            lines.append(f"- `{p}`: `{open(cmdf).read().strip()}`")
+            lines.append(f"- `{p}`: `{_repo_relative(open(cmdf).read().strip())}`")
     lines.append("")
     t = res.get("trace")
     if t:
@@ -299,6 +309,7 @@ def main(argv=None) -> int:
     s.add_argument("--md", default=None)
     s.add_argument("--json", default=None)
     s.add_argument("--title", default="rocprofv3 summary")
+    s.add_argument("--note", default=None, help="text placed under the title")
     s.add_argument("--record", default=None, help="JSON file to add this run's figures to (profiles/traffic.json)")
     s.add_argument("--key", default=None, help="entry name in --record, e.g. flux8k_r32")
     s.add_argument("--source", default=None, help="name of the Markdown summary the entry refers to")
@@ -315,7 +326,7 @@ def main(argv=None) -> int:
         passes = [p for p in a.passes.split(",") if p]
         return collect(a.out, cmd, passes, copy_cmd, a.timeout)
     res = summarize(a.root, a.kernel, a.flop, a.bytes, a.skip_first)
-    md = markdown(res, a.title)
+    md = markdown(res, a.title, a.note)
     if a.md:
         with open(a.md, "w") as f:
             f.write(md + "\n")

@@ -92,6 +92,7 @@ struct BwdBf16 {
   static constexpr int kPPR = D / 8;
   static constexpr int kRegion = kChunk * kRowBytes;  // bytes of one 32-row region
   static constexpr int kBlocks = kRegion / 1024;      // 1 KB direct-to-LDS blocks
+  static constexpr int kBlockPitch = 1024;            // copy block pitch
   static constexpr int kKK = D / 16;
   static constexpr int kNB = D / 32;
   static constexpr int kWavesPerSimd = 2;
@@ -186,6 +187,73 @@ struct BwdBf16 {
   }
 };
 
+// bf16, d = 128: the forward's granule layout.  A region is 8 blocks of 4
+// rows at a pitch of 1040 bytes (1 KB plus one 16-byte bank group of skew);
+// within a block, 32-column granule c of row j sits at bytes 256 c + 64 j, so
+// one copy instruction fills one block with coalesced 64-byte quads (lane l:
+// row (l / 4) % 4, piece 4 (l / 16) + l % 4) and no slot is padding.  Both
+// read patterns are conflict-free, and a piece's offset from the lane's first
+// piece is the same on every lane, so one lane address and immediate offsets
+// serve each product:
+//   row reads:       lane l, row l % 32, piece 2 kk + l / 32 -> granule kk / 2,
+//                    piece 2 (kk % 2) + l / 32 of it;
+//   transpose reads: rows 16 t + 8 h + 4 g + s / 4 sit 4 t + 2 h + g blocks in,
+//                    columns 32 nb + ... one granule (256 bytes) per nb.
+// Operand types, row loads and stores are those of BwdBf16<128>.
+struct BwdBf16G : BwdBf16<128> {
+  static constexpr int kBlockPitch = 1024 + 16;
+  static constexpr int kPitch = kBlockPitch;
+  static constexpr int kBlocks = kChunk / 4;
+  static constexpr int kRegion = kBlocks * kPitch;
+  static_assert(kBlocks % kWaves == 0, "regions split evenly over the wavefronts");
+
+  // LDS byte offset, within a region, of element `col` of chunk row `row`
+  __device__ static constexpr int lds_off(int row, int col) {
+    return (row / 4) * kPitch + 256 * (col / 32) + 64 * (row % 4) + 16 * ((col / 8) % 4) + 2 * (col % 8);
+  }
+  __device__ static bool slot_piece(int slot, int& r, int& p) {
+    const int b = slot >> 6, l = slot & 63;
+    r = 4 * b + ((l >> 2) & 3);
+    p = 4 * (l >> 4) + (l & 3);
+    return true;
+  }
+  __device__ static void row_mma(const char* region, int lane, const Rows& b, f32x16_t& acc) {
+    const char* a0 = region + lds_off(lane & 31, 8 * (lane >> 5));
+    acc = f32x16_t{};
+    for (int kk = 0; kk < kKK; ++kk) {
+      const bf16x8_t a = *(const bf16x8_t*)(a0 + 256 * (kk / 2) + 32 * (kk % 2));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b.x[kk], acc, 0, 0, 0);
+      if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __device__ static void row_mma_own(const char* region, const char* own, int lane, f32x16_t& acc) {
+    const int o = lds_off(lane & 31, 8 * (lane >> 5));
+    acc = f32x16_t{};
+    for (int kk = 0; kk < kKK; ++kk) {
+      const int e = o + 256 * (kk / 2) + 32 * (kk % 2);
+      const bf16x8_t a = *(const bf16x8_t*)(region + e);
+      const bf16x8_t b = *(const bf16x8_t*)(own + e);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+      if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __device__ static void tr_mma(const char* region, int lane, const Operand& w, f32x16_t* acc) {
+    const int g = lane >> 5, s = lane & 15, half = (lane >> 4) & 1;
+    const char* a00 = region + lds_off(4 * g + (s >> 2), 16 * half + 4 * (s & 3));
+    for (int t = 0; t < 2; ++t) {
+      for (int nb = 0; nb < kNB; ++nb) {
+        const char* a0 = a00 + 4 * t * kPitch + 256 * nb;
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds_char_t*)const_cast<char*>(a0));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(lds_char_t*)const_cast<char*>(a0 + 2 * kPitch));
+        const s16x8_t x = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, x), w.b[t], acc[nb], 0, 0, 0);
+        if (nb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+};
+
 // fp32: rows at a pitch of kPPR + 1 slots, no swizzle; v_mfma_f32_32x32x2_f32.
 template <int D>
 struct BwdF32 {
@@ -195,7 +263,8 @@ struct BwdF32 {
   static constexpr int kSlots = kPPR + 1;
   static constexpr int kPitch = kSlots * 16;
   static constexpr int kBlocks = (kChunk * kSlots + 64 * kWaves - 1) / (64 * kWaves) * kWaves;
-  static constexpr int kRegion = kBlocks * 1024;
+  static constexpr int kBlockPitch = 1024;
+  static constexpr int kRegion = kBlocks * kBlockPitch;
   static constexpr int kHalf = D / 2;
   static constexpr int kNB = D / 32;
   static constexpr int kWavesPerSimd = 1;
@@ -245,9 +314,10 @@ struct BwdF32 {
 // ---------------------------------------------------------------- staging
 //
 // Both gradient kernels stage two 32-row regions per chunk (dK/dV: Q and dO;
-// dQ: K and V) with direct-to-LDS buffer loads, as the forward does: one load
-// instruction of a wavefront fills one 1 KB block, lane l writing the 16-byte
-// slot 64 * block + l, and block b of a region is filled by wavefront b % 4.
+// dQ: K and V) with direct-to-LDS buffer loads issued in assembly (lds_copy),
+// as the forward does: one load instruction of a wavefront fills one 1 KB
+// block, lane l writing the 16-byte slot 64 * block + l (blocks
+// E::kBlockPitch apart), and block b of a region is filled by wavefront b % 4.
 // Each lane keeps the byte offset of its slot's piece from the chunk's first
 // token, for a dense token range and for a 4 x 8 cell tile (rows gw apart).
 // The key-centred kernel also stages the chunk's (lse2, D) pairs: one 4-byte
@@ -308,13 +378,14 @@ template <class E>
 __device__ __forceinline__ void stage_own(char* region, const char* head, int first, int n_tok, bool dense,
                                           int lane, int gw) {
   const int base = first < n_tok ? first : n_tok;
-  const __amdgpu_buffer_rsrc_t rs = byte_rsrc(head + (size_t)base * E::kRowBytes, bytes_left<E>(n_tok, first));
+  const u32x4_t rs = rsrc_words(head + (size_t)base * E::kRowBytes, bytes_left<E>(n_tok, first));
+  const uint32_t lds = lds_addr(region);
   for (int b = 0; b < E::kBlocks; ++b) {
     int r, pc;
     uint32_t off = kNoPiece;
     if (E::slot_piece(64 * b + lane, r, pc))
       off = (uint32_t)((dense ? r : ((r >> 3) * gw + (r & 7))) * E::kRowBytes + pc * 16);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(region + 1024 * b), 16, (int)off, 0, 0, 0);
+    lds_copy(lds + E::kBlockPitch * b, rs, off);
   }
 }
 
@@ -325,19 +396,16 @@ __device__ __forceinline__ void stage_bwd(char* st, const ChunkMeta& m, bool den
   const size_t base = (size_t)m.tok0 * E::kRowBytes;
   constexpr int kMaxLeft = 0x7fffffff / E::kRowBytes;  // a resource covers < 2 GB
   const uint32_t bytes = (uint32_t)(m.left < kMaxLeft ? m.left : kMaxLeft) * E::kRowBytes;
-  const __amdgpu_buffer_rsrc_t ra = byte_rsrc(abase + base, bytes), rb = byte_rsrc(bbase + base, bytes);
-  char* sa = st + BwdLayout<E>::kA + 1024 * wave;
-  char* sb = st + BwdLayout<E>::kB + 1024 * wave;
+  const u32x4_t ra = rsrc_words(abase + base, bytes), rb = rsrc_words(bbase + base, bytes);
+  const uint32_t sa = lds_addr(st) + BwdLayout<E>::kA + E::kBlockPitch * wave;
+  const uint32_t sb = lds_addr(st) + BwdLayout<E>::kB + E::kBlockPitch * wave;
   const uint32_t* off = dense ? pl.dense : pl.tile;
-  for (int i = 0; i < BwdPlan<E>::kPerWave; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(sa + 1024 * kWaves * i), 16, (int)off[i], 0, 0, 0);
-  for (int i = 0; i < BwdPlan<E>::kPerWave; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(sb + 1024 * kWaves * i), 16, (int)off[i], 0, 0, 0);
+  for (int i = 0; i < BwdPlan<E>::kPerWave; ++i) lds_copy(sa + E::kBlockPitch * kWaves * i, ra, off[i]);
+  for (int i = 0; i < BwdPlan<E>::kPerWave; ++i) lds_copy(sb + E::kBlockPitch * kWaves * i, rb, off[i]);
   if constexpr (STATS) {
-    const __amdgpu_buffer_rsrc_t rs = byte_rsrc((const char*)(sbase + (size_t)m.tok0 * 2),
-                                                (uint32_t)(m.left < 0x0fffffff ? m.left : 0x0fffffff) * 8);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(st + BwdLayout<E>::kStats + 256 * wave), 4,
-                                             (int)(dense ? pl.st_dense : pl.st_tile), 0, 0, 0);
+    const u32x4_t rs = rsrc_words((const char*)(sbase + (size_t)m.tok0 * 2),
+                                  (uint32_t)(m.left < 0x0fffffff ? m.left : 0x0fffffff) * 8);
+    lds_copy_dword(lds_addr(st) + BwdLayout<E>::kStats + 256 * wave, rs, dense ? pl.st_dense : pl.st_tile);
   }
   if (dense) asm volatile("; stage dense chunk");
   else asm volatile("; stage tile chunk");
@@ -716,7 +784,7 @@ int attn_bwd_launch(const BwdLaunch& a, void* stream) {
 
   int rc;
   if (a.dtype == CLEAR_BF16) {
-    rc = a.d == 128 ? launch_grads<BwdBf16<128>>(p, s, (int)grid) : launch_grads<BwdBf16<64>>(p, s, (int)grid);
+    rc = a.d == 128 ? launch_grads<BwdBf16G>(p, s, (int)grid) : launch_grads<BwdBf16<64>>(p, s, (int)grid);
   } else {
     rc = a.d == 128 ? launch_grads<BwdF32<128>>(p, s, (int)grid) : launch_grads<BwdF32<64>>(p, s, (int)grid);
   }

@@ -85,6 +85,34 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_rsrc(const char* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Buffer resource words (gfx9 layout, stride 0) over `bytes` bytes from a
+// uniform address: offsets at or past `bytes` read zeros.
+__device__ __forceinline__ u32x4_t rsrc_words(const char* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// One wavefront's direct-to-LDS copy of 64 x 16 bytes: lane l's piece at byte
+// voff of the resource lands at LDS address lds + 16 l.  Written in assembly so
+// that the compiler does not take it for a writer of the stage being read (it
+// cannot tell the two stages apart and would wait for the next chunk's copies
+// before the reads of the current one); the walk waits for the copies itself,
+// before each barrier (stage_barrier).
+__device__ __forceinline__ void lds_copy(uint32_t lds, const u32x4_t& rsrc, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(lds_char_t*)const_cast<char*>(p);
+}
+
+// As lds_copy, 64 x 4 bytes: lane l's word lands at lds + 4 l.
+__device__ __forceinline__ void lds_copy_dword(uint32_t lds, const u32x4_t& rsrc, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory");
+}
+
 // Per-chunk description, uniform: where the chunk's keys start, and what the
 // mask needs.
 struct ChunkMeta {

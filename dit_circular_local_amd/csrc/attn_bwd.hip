@@ -52,7 +52,7 @@ struct BwdParams {
   const char* k;
   const char* v;
   const char* dout;
-  const float* stats;  // [B*H][N][2]: (lse2, D)
+  const float* stats;  // [B*H][N][2]: (lse2, -D)
   char* dq;
   char* dk;
   char* dv;
@@ -74,8 +74,8 @@ struct BwdParams {
 //
 // An engine fixes the element type and how 32-row chunks sit in LDS, and
 // provides the two matrix-core patterns:
-//   row_mma: acc[m][n] = sum_k A[m][k] B[k][n], A = the chunk's rows m (LDS),
-//            B = the lane's own row n (VGPRs), k over d;
+//   row_mma: acc[m][n] = init[m][n] + sum_k A[m][k] B[k][n], A = the chunk's
+//            rows m (LDS), B = the lane's own row n (VGPRs), k over d;
 //   tr_mma:  acc[nb][d][n] += sum_m A[m][d] W[m][n], A = the chunk's rows read
 //            transposed (LDS), W = 32x32 accumulator values of this chunk
 //            (probabilities or dS) converted to an operand.
@@ -126,9 +126,10 @@ struct BwdBf16 {
       r.x[kk] = __builtin_bit_cast(bf16x8_t, valid ? x : u32x4_t{0, 0, 0, 0});
     }
   }
-  __device__ static void row_mma(const char* region, int lane, const Rows& b, f32x16_t& acc) {
+  __device__ static void row_mma(const char* region, int lane, const Rows& b, const f32x16_t& init,
+                                  f32x16_t& acc) {
     const int r = lane & 31, g = lane >> 5;
-    acc = f32x16_t{};
+    acc = init;
     for (int kk = 0; kk < kKK; ++kk) {
       const bf16x8_t a = *(const bf16x8_t*)(region + piece_at(r, 2 * kk + g));
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b.x[kk], acc, 0, 0, 0);
@@ -136,9 +137,10 @@ struct BwdBf16 {
     }
   }
   // as row_mma, with B read from the wavefront's own rows in LDS
-  __device__ static void row_mma_own(const char* region, const char* own, int lane, f32x16_t& acc) {
+  __device__ static void row_mma_own(const char* region, const char* own, int lane, const f32x16_t& init,
+                                      f32x16_t& acc) {
     const int r = lane & 31, g = lane >> 5;
-    acc = f32x16_t{};
+    acc = init;
     for (int kk = 0; kk < kKK; ++kk) {
       const bf16x8_t a = *(const bf16x8_t*)(region + piece_at(r, 2 * kk + g));
       const bf16x8_t b = *(const bf16x8_t*)(own + piece_at(r, 2 * kk + g));
@@ -217,24 +219,24 @@ struct BwdBf16G : BwdBf16<128> {
     p = 4 * (l >> 4) + (l & 3);
     return true;
   }
-  __device__ static void row_mma(const char* region, int lane, const Rows& b, f32x16_t& acc) {
+  __device__ static void row_mma(const char* region, int lane, const Rows& b, const f32x16_t& init,
+                                  f32x16_t& acc) {
     const char* a0 = region + lds_off(lane & 31, 8 * (lane >> 5));
-    acc = f32x16_t{};
+    acc = init;
     for (int kk = 0; kk < kKK; ++kk) {
       const bf16x8_t a = *(const bf16x8_t*)(a0 + 256 * (kk / 2) + 32 * (kk % 2));
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b.x[kk], acc, 0, 0, 0);
-      if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
     }
   }
-  __device__ static void row_mma_own(const char* region, const char* own, int lane, f32x16_t& acc) {
+  __device__ static void row_mma_own(const char* region, const char* own, int lane, const f32x16_t& init,
+                                      f32x16_t& acc) {
     const int o = lds_off(lane & 31, 8 * (lane >> 5));
-    acc = f32x16_t{};
+    acc = init;
     for (int kk = 0; kk < kKK; ++kk) {
       const int e = o + 256 * (kk / 2) + 32 * (kk % 2);
       const bf16x8_t a = *(const bf16x8_t*)(region + e);
       const bf16x8_t b = *(const bf16x8_t*)(own + e);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
-      if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
     }
   }
   __device__ static void tr_mma(const char* region, int lane, const Operand& w, f32x16_t* acc) {
@@ -288,15 +290,16 @@ struct BwdF32 {
       for (int e = 0; e < 4; ++e) r.x[4 * s4 + e] = valid ? x[e] : 0.0f;
     }
   }
-  __device__ static void row_mma(const char* region, int lane, const Rows& b, f32x16_t& acc) {
+  __device__ static void row_mma(const char* region, int lane, const Rows& b, const f32x16_t& init,
+                                  f32x16_t& acc) {
     const char* rb = region + (lane & 31) * kPitch + (lane >> 5) * kHalf * 4;
-    acc = f32x16_t{};
+    acc = init;
     for (int s4 = 0; s4 < kHalf / 4; ++s4) {
       const f32x4_t a = *(const f32x4_t*)(rb + s4 * 16);
       for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b.x[4 * s4 + e], acc, 0, 0, 0);
     }
   }
-  __device__ static void row_mma_own(const char*, const char*, int, f32x16_t&) {}
+  __device__ static void row_mma_own(const char*, const char*, int, const f32x16_t&, f32x16_t&) {}
   __device__ static void to_operand(const f32x16_t& e, Operand& w) { w.p = e; }
   __device__ static void tr_mma(const char* region, int lane, const Operand& w, f32x16_t* acc) {
     const int g = lane >> 5;
@@ -547,21 +550,26 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_bwd_dkd
       },
       [&](const ChunkInfo& c, const char* st) {
         if (!c.active) return;
-        f32x16_t s, dp;
-        E::row_mma(st + L::kA, lane, kr, s);
-        if constexpr (E::kOwnInLds) E::row_mma_own(st + L::kB, own_v, lane, dp);
-        else E::row_mma(st + L::kB, lane, vr, dp);
+        // dP - D: the product starts from -D of each query row (the staged
+        // statistics hold -D), so dS = P (dP - D) is one multiply
+        const float* sv = (const float*)(st + L::kStats + 256 * wave);
+        f32x16_t s, dp, nd;
+        for (int a = 0; a < 4; ++a) {
+          const f32x4_t x = *(const f32x4_t*)(sv + 32 + 8 * a + 4 * g);
+          for (int e = 0; e < 4; ++e) nd[4 * a + e] = x[e];
+        }
+        E::row_mma(st + L::kA, lane, kr, f32x16_t{}, s);
+        if constexpr (E::kOwnInLds) E::row_mma_own(st + L::kB, own_v, lane, nd, dp);
+        else E::row_mma(st + L::kB, lane, vr, nd, dp);
         if (c.coord && c.inside && mt.tbl != nullptr)
           apply_lane_masks(s, mt.tbl + ((c.kty * (2 * mt.kx + 1) + c.ktx + mt_base) << 4));
         else mask_chunk(s, c, ks, g, w.cy, w.cx, p.r2);
-        const float* sv = (const float*)(st + L::kStats + 256 * wave);
         for (int a = 0; a < 4; ++a) {
           const f32x4_t l2 = *(const f32x4_t*)(sv + 8 * a + 4 * g);
-          const f32x4_t dd = *(const f32x4_t*)(sv + 32 + 8 * a + 4 * g);
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * a + e;
             s[i] = __builtin_amdgcn_exp2f(fmaf(s[i], p.scale_log2, -l2[e]));
-            dp[i] = s[i] * (dp[i] - dd[e]);
+            dp[i] = s[i] * dp[i];
           }
         }
         typename E::Operand op;
@@ -608,7 +616,9 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_bwd_dq_
   const size_t own = (size_t)own_tok * E::kRowBytes;
   E::load_rows(p.q + head_off + own, w.valid, g, qr);
   E::load_rows(p.dout + head_off + own, w.valid, g, dor);
-  const float2 stq = *(const float2*)(p.stats + ((size_t)w.bh * p.N + own_tok) * 2);
+  const float2 stq = *(const float2*)(p.stats + ((size_t)w.bh * p.N + own_tok) * 2);  // (lse2, -D)
+  f32x16_t nd;
+  for (int i = 0; i < 16; ++i) nd[i] = stq.y;
   f32x16_t dq[E::kNB];
   for (int nb = 0; nb < E::kNB; ++nb) dq[nb] = f32x16_t{};
 
@@ -623,14 +633,14 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_bwd_dq_
       [&](const ChunkInfo& c, const char* st) {
         if (!c.active) return;
         f32x16_t s, dp;
-        E::row_mma(st + L::kA, lane, qr, s);
-        E::row_mma(st + L::kB, lane, dor, dp);
+        E::row_mma(st + L::kA, lane, qr, f32x16_t{}, s);
+        E::row_mma(st + L::kB, lane, dor, nd, dp);  // dP - D of the lane's query
         if (c.coord && c.inside && mt.tbl != nullptr)
           apply_lane_masks(s, mt.tbl + ((c.kty * (2 * mt.kx + 1) + c.ktx + mt_base) << 4));
         else mask_chunk(s, c, ks, g, w.cy, w.cx, p.r2);
         for (int i = 0; i < 16; ++i) {
           const float pr = __builtin_amdgcn_exp2f(fmaf(s[i], p.scale_log2, -stq.x));
-          dp[i] = pr * (dp[i] - stq.y);
+          dp[i] = pr * dp[i];
         }
         typename E::Operand op;
         E::to_operand(dp, op);
@@ -656,8 +666,9 @@ struct PrepArgs {
   long long rows;  // B*H*N
 };
 
-// 16 threads per row, 16 rows per 256-thread workgroup: D_i = dO_i . O_i in
-// fp32 and lse2_i = lse_i * log2(e).
+// 16 threads per row, 16 rows per 256-thread workgroup: lse2_i = lse_i *
+// log2(e) and -D_i = -(dO_i . O_i) in fp32 (the gradient kernels start the dP
+// products from -D).
 template <int D, bool BF16>
 __global__ void __launch_bounds__(256) clear_attn_bwd_prep_kernel(PrepArgs a) {
   constexpr int kPer = D / 16;  // elements per thread
@@ -679,7 +690,7 @@ __global__ void __launch_bounds__(256) clear_attn_bwd_prep_kernel(PrepArgs a) {
   for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
   if (row < a.rows && sub == 0) {
     a.stats[2 * row] = a.lse[row] * 1.4426950408889634f;
-    a.stats[2 * row + 1] = acc;
+    a.stats[2 * row + 1] = -acc;
   }
 }
 

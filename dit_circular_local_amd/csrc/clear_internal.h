@@ -95,7 +95,7 @@ struct BwdLaunch {
   void* dq;
   void* dk;
   void* dv;
-  float* ws_stats;    // [B*H][N][2]: (lse * log2(e), dO . O)
+  float* ws_stats;    // [B*H][N][2]: (lse * log2(e), -(dO . O))
   float* ws_dq;       // text partials [splits][B*H][n_text][d]   (n_text > 0)
   float* ws_dk;
   float* ws_dv;

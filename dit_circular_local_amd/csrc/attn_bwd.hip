@@ -542,8 +542,8 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_bwd_dkd
   const BwdPlan<E> plan = make_bwd_plan<E>(wave, lane, p.gw);
   const MaskTable mt{(const_u64_t*)p.mask_tbl, p.mt_ky, p.mt_kx};
   const int mt_base = table_base(mt, w.sy0, w.sx0);
-  // one key tile per trip: two per trip spill this kernel's registers in the loop
-  walk_chunks<Walk::kSplit>(
+  // two key tiles per trip (the stages and descriptors in flight keep fixed roles)
+  walk_chunks(
       ks, n, wave, smem, smem + L::kStageABS,
       [&](char* st, const ChunkMeta& m, bool dense) {
         stage_bwd<E, true>(st, m, dense, wave, qbase, obase, sbase, plan);
@@ -625,7 +625,7 @@ __global__ void __launch_bounds__(kThreads, E::kWavesPerSimd) clear_attn_bwd_dq_
   const BwdPlan<E> plan = make_bwd_plan<E>(wave, lane, p.gw);
   const MaskTable mt{(const_u64_t*)p.mask_tbl, p.mt_ky, p.mt_kx};
   const int mt_base = table_base(mt, w.sy0, w.sx0);
-  walk_chunks<Walk::kSplitPairs>(
+  walk_chunks(
       ks, n, wave, smem, smem + L::kStageAB,
       [&](char* st, const ChunkMeta& m, bool dense) {
         stage_bwd<E, false>(st, m, dense, wave, kbase, vbase, nullptr, plan);

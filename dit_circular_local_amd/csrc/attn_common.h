@@ -194,11 +194,9 @@ __device__ __forceinline__ void stage_barrier() {
 // a loop of its own that carries only its own state and tests, and the key
 // tiles go two per trip so that the stages and the two descriptors in flight
 // keep fixed roles: in tile_step, mc describes chunk jj (in cur), mn chunk
-// jj + 1 (copied to nxt), and mc then receives chunk jj + 2.  Walk::kSplit
-// keeps one key tile per trip (less code, where registers are scarce).
-enum class Walk { kSplit, kSplitPairs };
-
-template <Walk kWalk = Walk::kSplitPairs, class Stage, class Compute>
+// jj + 1 (copied to nxt), and mc then receives chunk jj + 2.  The dense loop
+// also goes two chunks per trip; its odd last chunk swaps the roles.
+template <class Stage, class Compute>
 __device__ __forceinline__ void walk_chunks(const KeySource& ks, int n, int wave, char* st_cur, char* st_nxt,
                                             Stage&& stage, Compute&& compute) {
   if (n <= 0) return;
@@ -213,11 +211,9 @@ __device__ __forceinline__ void walk_chunks(const KeySource& ks, int n, int wave
     compute(c, cur);
   };
   int j = 0;
-  if constexpr (kWalk == Walk::kSplitPairs) {
-    for (; j + 1 < ks.n_dense; j += 2) {
-      dense_step(j, m_cur, m_nxt, st_cur, st_nxt);
-      dense_step(j + 1, m_nxt, m_cur, st_nxt, st_cur);
-    }
+  for (; j + 1 < ks.n_dense; j += 2) {
+    dense_step(j, m_cur, m_nxt, st_cur, st_nxt);
+    dense_step(j + 1, m_nxt, m_cur, st_nxt, st_cur);
   }
   for (; j < ks.n_dense; ++j) {
     dense_step(j, m_cur, m_nxt, st_cur, st_nxt);  // m_cur now describes chunk j + 2
@@ -235,25 +231,12 @@ __device__ __forceinline__ void walk_chunks(const KeySource& ks, int n, int wave
     mc = tile_chunk_meta(ks, jj + 2 < n ? jj + 2 : n - 1);
     compute(c, cur);
   };
-  if constexpr (kWalk == Walk::kSplitPairs) {
-    for (; j + 1 < n; j += 2) {
-      tile_step(j, m_cur, m_nxt, st_cur, st_nxt);
-      tile_step(j + 1, m_nxt, m_cur, st_nxt, st_cur);
-    }
-    if (j < n) tile_step(j, m_cur, m_nxt, st_cur, st_nxt);
-  } else {
-    for (; j < n; ++j) {
-      tile_step(j, m_cur, m_nxt, st_cur, st_nxt);  // m_cur now describes chunk j + 2
-      const ChunkMeta m = m_cur;
-      m_cur = m_nxt;
-      m_nxt = m;
-      char* t = st_cur;
-      st_cur = st_nxt;
-      st_nxt = t;
-    }
+  for (; j + 1 < n; j += 2) {
+    tile_step(j, m_cur, m_nxt, st_cur, st_nxt);
+    tile_step(j + 1, m_nxt, m_cur, st_nxt, st_cur);
   }
+  if (j < n) tile_step(j, m_cur, m_nxt, st_cur, st_nxt);
 }
-
 
 // The lane-mask table of partly admitted chunks (built on the host next to
 // the tile map): for a chunk tile at offset (dy, dx) = (4 iy, 8 ix) from the

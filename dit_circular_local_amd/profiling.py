@@ -253,40 +253,46 @@ def _repo_relative(cmd: str) -> str:
     return re.sub(r"/\S*?/repo(?=/)", "$REPO", cmd)
 
 
-def markdown(res: dict, title: str, note: Optional[str] = None) -> str:
-    """A short Markdown summary of ``summarize``'s record."""
+def markdown(res, title: str, note: Optional[str] = None) -> str:
+    """A short Markdown summary of ``summarize``'s record, or of several
+    records of one run (one section per kernel)."""
+    recs = [res] if isinstance(res, dict) else list(res)
     lines = [f"# {title}", ""]
     if note:
         lines += [note, ""]
     lines += ["Commands (each pass its own profiler run, from /tmp; `$REPO` is the repository root):", ""]
     for p in ("trace", "sq", "sq2", "fetch", "write", "copy_fetch", "copy_write"):
-        cmdf = os.path.join(res["root"], f"{p}.cmd")
+        cmdf = os.path.join(recs[0]["root"], f"{p}.cmd")
         if os.path.exists(cmdf):
             lines.append(f"- `{p}`: `{_repo_relative(open(cmdf).read().strip())}`")
     lines.append("")
-    t = res.get("trace")
-    if t:
-        lines += ["| kernel | dispatches | mean ms (timed) | min ms | max ms |", "|---|---|---|---|---|",
-                  f"| {res['kernel']} | {t['dispatches']} | {t['mean_ms']:.4f} | {t['min_ms']:.4f} | "
-                  f"{t['max_ms']:.4f} |", ""]
+    if recs[0].get("kernels"):
         lines += ["All kernels of the run:", "", "| kernel | dispatches | mean ms |", "|---|---|---|"]
-        for k, v in sorted(res["kernels"].items(), key=lambda kv: -kv[1]["mean_ms"] * kv[1]["dispatches"]):
+        for k, v in sorted(recs[0]["kernels"].items(), key=lambda kv: -kv[1]["mean_ms"] * kv[1]["dispatches"]):
             lines.append(f"| `{k[:90]}` | {v['dispatches']} | {v['mean_ms']:.4f} |")
         lines.append("")
-    if res["counters"]:
-        lines += ["| counter | per dispatch |", "|---|---|"]
-        lines += [f"| {k} | {v:.4g} |" for k, v in sorted(res["counters"].items())]
-        lines.append("")
-    d = res["derived"]
-    if d:
-        lines += ["| derived | value |", "|---|---|"]
-        for k, v in d.items():
-            if isinstance(v, dict):
-                for kk, vv in v.items():
-                    lines.append(f"| {k}.{kk} | {vv:.4g} |")
-            else:
-                lines.append(f"| {k} | {v:.4g} |")
-        lines.append("")
+    for rec in recs:
+        if len(recs) > 1:
+            lines += [f"## {rec['kernel']}", ""]
+        t = rec.get("trace")
+        if t:
+            lines += ["| kernel | dispatches | mean ms (timed) | min ms | max ms |", "|---|---|---|---|---|",
+                      f"| {rec['kernel']} | {t['dispatches']} | {t['mean_ms']:.4f} | {t['min_ms']:.4f} | "
+                      f"{t['max_ms']:.4f} |", ""]
+        if rec["counters"]:
+            lines += ["| counter | per dispatch |", "|---|---|"]
+            lines += [f"| {k} | {v:.4g} |" for k, v in sorted(rec["counters"].items())]
+            lines.append("")
+        d = rec["derived"]
+        if d:
+            lines += ["| derived | value |", "|---|---|"]
+            for k, v in d.items():
+                if isinstance(v, dict):
+                    for kk, vv in v.items():
+                        lines.append(f"| {k}.{kk} | {vv:.4g} |")
+                else:
+                    lines.append(f"| {k} | {v:.4g} |")
+            lines.append("")
     return "\n".join(lines)
 
 
@@ -302,9 +308,13 @@ def main(argv=None) -> int:
     c.add_argument("command", nargs=argparse.REMAINDER)
     s = sub.add_parser("summarize", help="reduce collected CSVs (anywhere)")
     s.add_argument("root")
-    s.add_argument("--kernel", default="clear_attn_fwd_kernel")
-    s.add_argument("--flop", type=float, default=None, help="algorithmic flops per dispatch")
-    s.add_argument("--bytes", type=float, default=None, help="algorithmic bytes per dispatch")
+    s.add_argument("--kernel", action="append", default=None,
+                   help="kernel name (substring); repeat for several kernels of one run "
+                        "(default clear_attn_fwd_kernel)")
+    s.add_argument("--flop", type=float, action="append", default=None,
+                   help="algorithmic flops per dispatch (one per --kernel)")
+    s.add_argument("--bytes", type=float, action="append", default=None,
+                   help="algorithmic bytes per dispatch (one per --kernel)")
     s.add_argument("--skip-first", type=int, default=1)
     s.add_argument("--md", default=None)
     s.add_argument("--json", default=None)
@@ -325,7 +335,15 @@ def main(argv=None) -> int:
                 copy_cmd = [cmd[0], bench[0], "--copy-probe-mib", str(a.copy_mib)]
         passes = [p for p in a.passes.split(",") if p]
         return collect(a.out, cmd, passes, copy_cmd, a.timeout)
-    res = summarize(a.root, a.kernel, a.flop, a.bytes, a.skip_first)
+    kernels = a.kernel or ["clear_attn_fwd_kernel"]
+    flops = a.flop or [None] * len(kernels)
+    nbytes = a.bytes or [None] * len(kernels)
+    if len(flops) != len(kernels) or len(nbytes) != len(kernels):
+        ap.error("give --flop and --bytes once per --kernel (or not at all)")
+    recs = [summarize(a.root, k, f, b, a.skip_first) for k, f, b in zip(kernels, flops, nbytes)]
+    if a.record and len(recs) != 1:
+        ap.error("--record takes one kernel")
+    res = recs[0] if len(recs) == 1 else recs
     md = markdown(res, a.title, a.note)
     if a.md:
         with open(a.md, "w") as f:

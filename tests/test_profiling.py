@@ -96,3 +96,21 @@ def test_pass_commands_put_the_program_after_the_separator():
         sq = [c for c in cs if c.startswith("SQ_")]
         grbm = [c for c in cs if c.startswith("GRBM_")]
         assert len(sq) <= 8 and len(grbm) <= 2, name
+
+
+def test_one_summary_for_several_kernels_of_a_run(tmp_path):
+    root = str(tmp_path)
+    ka = "void clear::(anonymous namespace)::clear_attn_bwd_dkdv_kernel<X>(P)"
+    kb = "void clear::(anonymous namespace)::clear_attn_bwd_dq_kernel<X>(P)"
+    th = ["Kind", "Agent_Id", "Queue_Id", "Stream_Id", "Thread_Id", "Dispatch_Id", "Kernel_Id", "Kernel_Name",
+          "Correlation_Id", "Start_Timestamp", "End_Timestamp"]
+    rows = []
+    for i in range(3):
+        rows.append(["KERNEL_DISPATCH", "Agent 1", 1, 0, 1, 2 * i, 1, ka, 2 * i, 0, 30e6])
+        rows.append(["KERNEL_DISPATCH", "Agent 1", 1, 0, 1, 2 * i + 1, 2, kb, 2 * i + 1, 0, 20e6])
+    _write(os.path.join(root, "trace", "trace_kernel_trace.csv"), th, rows)
+    recs = [P.summarize(root, k, flop=None, alg_bytes=None) for k in ("bwd_dkdv", "bwd_dq")]
+    assert abs(recs[0]["trace"]["mean_ms"] - 30.0) < 1e-9 and abs(recs[1]["trace"]["mean_ms"] - 20.0) < 1e-9
+    md = P.markdown(recs, "t", "note")
+    assert md.count("## ") == 2 and "All kernels of the run" in md and "note" in md
+    assert md.index("## bwd_dkdv") < md.index("## bwd_dq")

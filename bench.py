@@ -228,15 +228,25 @@ def _oracle_worker(args):
     """One worker of the CPU baseline: regenerates its head of the workload from
     the seeded generator, waits for the others, then runs the fp64 oracle on
     text rows and whole rows of 8x8 image blocks until its time budget is spent.
-    Returns (admitted pairs, text rows, block rows, seconds of oracle work)."""
+    Returns (admitted pairs, text rows, block rows, seconds of oracle work,
+    BLAS threads of the worker)."""
     (wname, seed, head, radius, budget_s, first_block_row, barrier) = args
-    try:
-        from threadpoolctl import threadpool_limits
-        threadpool_limits(1)
-    except Exception:
-        pass
     from dit_circular_local_amd.inputs import WORKLOADS, make_head
     from oracle import attention_head, in_window_pairs
+
+    # one BLAS thread per worker; the limit applies to the libraries already
+    # loaded, so it comes after the imports that load numpy's BLAS (the pool's
+    # environment sets the thread counts to 1 as well)
+    blas_threads = None
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threadpool_limits(1)
+        blas_threads = max((i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"),
+                           default=None)
+    except Exception:
+        pass
+    import torch
+    torch.set_num_threads(1)
 
     w = WORKLOADS[wname]
     # widened to float64 here, outside the timed region (the oracle would otherwise
@@ -258,7 +268,7 @@ def _oracle_worker(args):
         rows_done += 1
     secs = time.perf_counter() - t0
     pairs = in_window_pairs(w.n_text, w.grid_h, w.grid_w, r2, text_rows=text_rows, blocks=blocks)
-    return pairs, len(text_rows), rows_done, secs
+    return pairs, len(text_rows), rows_done, secs, blas_threads
 
 
 def cpu_baseline(w, radius, budget_s, seed=0):
@@ -275,11 +285,25 @@ def cpu_baseline(w, radius, budget_s, seed=0):
     workers = max(1, min(ncpu, 16))
     nby = -(-w.grid_h // 8)
     ctx = mp.get_context("spawn")  # the parent holds a GPU context: never fork it
-    with ctx.Manager() as mgr:
-        barrier = mgr.Barrier(workers)
-        jobs = [(w.name, seed, i % w.H, radius, budget_s, (i * nby) // workers, barrier) for i in range(workers)]
-        with ctx.Pool(workers) as pool:
-            res = pool.map(_oracle_worker, jobs)
+    # the workers inherit the environment when they start: one BLAS / OpenMP
+    # thread each (hosts may set these to the core count, and 16 workers x 16
+    # spinning BLAS threads on 16 cores starve every worker)
+    keys = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+    saved = {k: os.environ.get(k) for k in keys}
+    os.environ.update({k: "1" for k in keys})
+    try:
+        with ctx.Manager() as mgr:
+            barrier = mgr.Barrier(workers)
+            jobs = [(w.name, seed, i % w.H, radius, budget_s, (i * nby) // workers, barrier)
+                    for i in range(workers)]
+            with ctx.Pool(workers) as pool:
+                res = pool.map(_oracle_worker, jobs)
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
     pairs = sum(r[0] for r in res)
     secs = max(r[3] for r in res)
     tflops = 4.0 * w.d * pairs / secs / 1e12
@@ -295,7 +319,7 @@ def cpu_baseline(w, radius, budget_s, seed=0):
         "seconds": secs,
         "os_cpu_count": ncpu,
         "worker_processes": workers,
-        "blas_threads_per_worker": 1,
+        "blas_threads_per_worker": max((r[4] for r in res if r[4] is not None), default=None),
         "radius": radius,
         "full_layer_seconds_extrapolated": layer_flops / (tflops * 1e12),
     }

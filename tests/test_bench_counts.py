@@ -43,3 +43,19 @@ def test_computed_work_covers_every_admitted_pair(n_text, gh, gw, r2, window):
     import dit_circular_local_amd as ca
 
     assert bench.computed_pairs(ca, n_text, gh, gw, r2, window) >= bench.admitted_pairs(n_text, gh, gw, r2, window)
+
+
+def test_cpu_baseline_workers_run_one_blas_thread_each(monkeypatch):
+    # hosts may export BLAS / OpenMP thread counts equal to the core count; the
+    # pool's workers must still run one thread each, and the parent's
+    # environment must come back unchanged
+    from dit_circular_local_amd.inputs import WORKLOADS
+
+    for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        monkeypatch.setenv(k, "16")
+    r = bench.cpu_baseline(WORKLOADS["tiny"], 4, 0.5)
+    assert r["blas_threads_per_worker"] == 1
+    assert r["value"] > 0 and r["worker_processes"] >= 1 and r["kind"] == "oracle"
+    assert " 0 block rows" not in r["sample"]
+    import os
+    assert all(os.environ[k] == "16" for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"))

@@ -224,13 +224,33 @@ def time_backward(ca, torch, q, k, v, w, radius, steps, warmup):
     return ms[len(ms) // 2], sum(ms) / len(ms)
 
 
+def _oracle_units(w, index, workers, text_group=64):
+    """Work units of one head for worker `index` of `workers`: groups of up to
+    `text_group` text rows and whole rows of 8x8 image blocks, interleaved in
+    proportion (any prefix holds about the same share of each), each worker
+    starting at another place so that the pool covers different parts."""
+    ntg = -(-w.n_text // text_group) if w.n_text > 0 else 0
+    nby, nbx = -(-w.grid_h // 8), -(-w.grid_w // 8)
+    units = []
+    for t in range(ntg):
+        g = (t + index * ntg // workers) % ntg
+        rows = list(range(g * text_group, min(w.n_text, (g + 1) * text_group)))
+        units.append(((t + 0.5) / ntg, "text", rows))
+    for b in range(nby):
+        by = (b + index * nby // workers) % nby
+        units.append(((b + 0.5) / nby, "blocks", [(by, bx) for bx in range(nbx)]))
+    units.sort(key=lambda u: u[0])
+    return [(kind, payload) for _, kind, payload in units]
+
+
 def _oracle_worker(args):
-    """One worker of the CPU baseline: regenerates its head of the workload from
-    the seeded generator, waits for the others, then runs the fp64 oracle on
-    text rows and whole rows of 8x8 image blocks until its time budget is spent.
-    Returns (admitted pairs, text rows, block rows, seconds of oracle work,
-    BLAS threads of the worker)."""
-    (wname, seed, head, radius, budget_s, first_block_row, barrier) = args
+    """One worker of the CPU baseline.  For each job (workload, radius, time
+    budget) in turn: regenerate head `index` mod H of the workload from the
+    seeded generator, widen it to float64, wait for the other workers, then run
+    the fp64 oracle over the head's work units until the head is done or the
+    budget is spent.  Returns per job (admitted pairs, text rows, block rows,
+    seconds, units done, units), and the BLAS threads of the worker."""
+    (jobs, seed, index, workers, barrier) = args
     from dit_circular_local_amd.inputs import WORKLOADS, make_head
     from oracle import attention_head, in_window_pairs
 
@@ -248,42 +268,50 @@ def _oracle_worker(args):
     import torch
     torch.set_num_threads(1)
 
-    w = WORKLOADS[wname]
-    # widened to float64 here, outside the timed region (the oracle would otherwise
-    # widen the whole head again on every call)
-    qh, kh, vh = (make_head(w.n, w.d, t, 0, head, seed, w.dtype, w.rms_norm, w.scale).double().numpy()
-                  for t in ("q", "k", "v"))
-    r2 = radius * radius
-    nby, nbx = -(-w.grid_h // 8), -(-w.grid_w // 8)
-    text_rows = list(range((16 * head) % w.n_text, (16 * head) % w.n_text + 16)) if w.n_text >= 16 else []
-    barrier.wait()
-    t0 = time.perf_counter()
-    attention_head(qh, kh, vh, w.n_text, w.grid_h, w.grid_w, r2, text_rows=text_rows, blocks=[])
-    blocks, rows_done = [], 0
-    while time.perf_counter() - t0 < budget_s and rows_done < nby:
-        by = (first_block_row + rows_done) % nby
-        row = [(by, bx) for bx in range(nbx)]
-        attention_head(qh, kh, vh, w.n_text, w.grid_h, w.grid_w, r2, text_rows=[], blocks=row)
-        blocks += row
-        rows_done += 1
-    secs = time.perf_counter() - t0
-    pairs = in_window_pairs(w.n_text, w.grid_h, w.grid_w, r2, text_rows=text_rows, blocks=blocks)
-    return pairs, len(text_rows), rows_done, secs, blas_threads
+    out = []
+    for wname, radius, budget_s in jobs:
+        w = WORKLOADS[wname]
+        head = index % w.H
+        # widened to float64 here, outside the timed region (the oracle would
+        # otherwise widen the whole head again on every call)
+        qh, kh, vh = (make_head(w.n, w.d, t, 0, head, seed, w.dtype, w.rms_norm, w.scale).double().numpy()
+                      for t in ("q", "k", "v"))
+        r2 = radius * radius
+        units = _oracle_units(w, index, workers)
+        text_rows, blocks, done = [], [], 0
+        barrier.wait()
+        t0 = time.perf_counter()
+        for kind, payload in units:
+            if done and time.perf_counter() - t0 >= budget_s:
+                break
+            if kind == "text":
+                attention_head(qh, kh, vh, w.n_text, w.grid_h, w.grid_w, r2, text_rows=payload, blocks=[])
+                text_rows += payload
+            else:
+                attention_head(qh, kh, vh, w.n_text, w.grid_h, w.grid_w, r2, text_rows=[], blocks=payload)
+                blocks += payload
+            done += 1
+        secs = time.perf_counter() - t0
+        pairs = in_window_pairs(w.n_text, w.grid_h, w.grid_w, r2, text_rows=text_rows, blocks=blocks)
+        out.append((pairs, len(text_rows), len(blocks) // max(1, -(-w.grid_w // 8)), secs, done, len(units)))
+        del qh, kh, vh
+    return out, blas_threads
 
 
-def cpu_baseline(w, radius, budget_s, seed=0):
-    """The fp64 oracle, untuned, on a bounded sample of the same layer, over a
-    process pool on the host's cores (one BLAS thread per worker): worker i
-    takes head i (mod H), 16 of its text rows and whole rows of 8x8 image
-    blocks (spread over the grid) until `budget_s` seconds of oracle work are
-    spent.  Reported in the metric's unit: 4 d x admitted pairs / the slowest
-    worker's seconds (the workers run at once), with the full layer's time at
-    that rate as an extrapolation."""
+def cpu_oracle_runs(jobs, seed=0):
+    """The fp64 oracle, untuned, over a process pool on the host's cores: one
+    worker per core (at most 16), one BLAS thread each, every worker on its own
+    head.  `jobs` is a list of (workload, radius, seconds): the workers take the
+    jobs in order, all at once (a barrier starts each job), each running whole
+    heads where the budget allows and a proportional sample of text-row groups
+    and image block rows where it does not.  Returns one record per job, in the
+    metric's unit: 4 d x admitted pairs covered / the slowest worker's seconds."""
     import multiprocessing as mp
+
+    from dit_circular_local_amd.inputs import WORKLOADS
 
     ncpu = os.cpu_count() or 1
     workers = max(1, min(ncpu, 16))
-    nby = -(-w.grid_h // 8)
     ctx = mp.get_context("spawn")  # the parent holds a GPU context: never fork it
     # the workers inherit the environment when they start: one BLAS / OpenMP
     # thread each (hosts may set these to the core count, and 16 workers x 16
@@ -294,35 +322,52 @@ def cpu_baseline(w, radius, budget_s, seed=0):
     try:
         with ctx.Manager() as mgr:
             barrier = mgr.Barrier(workers)
-            jobs = [(w.name, seed, i % w.H, radius, budget_s, (i * nby) // workers, barrier)
-                    for i in range(workers)]
+            args = [(list(jobs), seed, i, workers, barrier) for i in range(workers)]
             with ctx.Pool(workers) as pool:
-                res = pool.map(_oracle_worker, jobs)
+                res = pool.map(_oracle_worker, args)
     finally:
         for k, v in saved.items():
             if v is None:
                 os.environ.pop(k, None)
             else:
                 os.environ[k] = v
-    pairs = sum(r[0] for r in res)
-    secs = max(r[3] for r in res)
-    tflops = 4.0 * w.d * pairs / secs / 1e12
-    layer_flops = 4.0 * w.d * admitted_pairs(w.n_text, w.grid_h, w.grid_w, radius * radius) * w.B * w.H
-    return {
-        "value": tflops,
-        "unit": "TFLOP/s",
-        "cores": workers,
-        "kind": "oracle",
-        "sample": f"{workers} worker processes, one per head {sorted(set(j % w.H for j in range(workers)))}: "
-                  f"16 text rows and whole rows of 8x8 image blocks each ({sum(r[2] for r in res)} block rows "
-                  f"of {nby}) for ~{budget_s:.0f} s, r={radius}; {pairs} admitted pairs in {secs:.1f} s; fp64 numpy",
-        "seconds": secs,
-        "os_cpu_count": ncpu,
-        "worker_processes": workers,
-        "blas_threads_per_worker": max((r[4] for r in res if r[4] is not None), default=None),
-        "radius": radius,
-        "full_layer_seconds_extrapolated": layer_flops / (tflops * 1e12),
-    }
+    blas = max((b for _, b in res if b is not None), default=None)
+    records = []
+    for j, (wname, radius, budget_s) in enumerate(jobs):
+        w = WORKLOADS[wname]
+        per = [r[0][j] for r in res]
+        pairs = sum(x[0] for x in per)
+        secs = max(x[3] for x in per)
+        tflops = 4.0 * w.d * pairs / secs / 1e12 if secs > 0 else None
+        whole = all(x[4] == x[5] for x in per)
+        heads = sorted(set(i % w.H for i in range(workers)))
+        layer_flops = 4.0 * w.d * admitted_pairs(w.n_text, w.grid_h, w.grid_w, radius * radius) * w.B * w.H
+        nby = -(-w.grid_h // 8)
+        records.append({
+            "value": tflops,
+            "unit": "TFLOP/s",
+            "cores": workers,
+            "kind": "oracle",
+            "sample": (f"{workers} worker processes on heads {heads}: "
+                       + ("each its whole head" if whole else
+                          f"each a proportional share of its head's groups of 64 text rows and rows of 8x8 image "
+                          f"blocks for ~{budget_s:g} s ({sum(x[1] for x in per)} text rows, "
+                          f"{sum(x[2] for x in per)} block rows of {nby} per head, over all workers)")
+                       + f", r={radius}; {pairs} admitted pairs in {secs:.2f} s; fp64 numpy"),
+            "seconds": secs,
+            "whole_heads": whole,
+            "os_cpu_count": ncpu,
+            "worker_processes": workers,
+            "blas_threads_per_worker": blas,
+            "radius": radius,
+            "full_layer_seconds_extrapolated": layer_flops / (tflops * 1e12) if tflops else None,
+        })
+    return records
+
+
+def cpu_baseline(w, radius, budget_s, seed=0):
+    """The CPU baseline of one workload at one radius (see cpu_oracle_runs)."""
+    return cpu_oracle_runs([(w.name, radius, budget_s)], seed)[0]
 
 
 def time_configs(ca, torch, steps=5, warmup=2):
@@ -367,6 +412,8 @@ def main():
                     help="also time the backward (clear_attn_bwd) at these radii ('' : none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="oracle work per worker and radius for the CPU baseline")
+    ap.add_argument("--cpu-config-seconds", type=float, default=4.0,
+                    help="oracle work per worker for each other configuration (at most a whole head)")
     ap.add_argument("--no-configs", action="store_true", help="skip timing the other workload configurations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -529,11 +576,23 @@ def main():
     if not args.no_cpu_baseline:
         del q, k, v
         torch.cuda.empty_cache()
-        for r in radii:
-            log(f"timing the CPU oracle on a sample, r={r} (~{args.cpu_seconds:.0f} s per worker)...")
-            cb = cpu_baseline(w, r, args.cpu_seconds)
+        from dit_circular_local_amd.inputs import WORKLOADS as _W
+
+        jobs = [(w.name, r, args.cpu_seconds) for r in radii]
+        if "configs" in line:
+            jobs += [(name, r, args.cpu_config_seconds) for name in ("tiny", "flux1k", "flux2k", "flux4k", "flux8k")
+                     for r in _W[name].radii]
+        log(f"timing the CPU oracle: {len(jobs)} runs ({args.cpu_seconds:.0f} s per worker at the headline "
+            f"radii, {args.cpu_config_seconds:.0f} s per configuration or a whole head)...")
+        recs = cpu_oracle_runs(jobs)
+        for (name, r, _), cb in zip(jobs[:len(radii)], recs):
             line["cpu_baseline" if r == main_r else f"cpu_baseline_r{r}"] = cb
             log(f"CPU oracle r={r}: {cb['value']:.4f} TFLOP/s on {cb['worker_processes']} processes")
+        for (name, r, _), cb in zip(jobs[len(radii):], recs[len(radii):]):
+            line["configs"][f"{name}_r{r}"]["cpu_oracle"] = {
+                k: cb[k] for k in ("value", "unit", "seconds", "whole_heads", "worker_processes", "sample")}
+            ratio = line["configs"][f"{name}_r{r}"]["in_window_tflops"] / cb["value"] if cb["value"] else None
+            line["configs"][f"{name}_r{r}"]["gpu_over_cpu_oracle"] = round(ratio, 1) if ratio else None
     print(json.dumps(line), flush=True)
 
 

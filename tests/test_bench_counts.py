@@ -59,3 +59,34 @@ def test_cpu_baseline_workers_run_one_blas_thread_each(monkeypatch):
     assert " 0 block rows" not in r["sample"]
     import os
     assert all(os.environ[k] == "16" for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"))
+
+
+def test_cpu_oracle_runs_report_whole_heads_and_samples():
+    # a whole head where the budget allows it, a proportional sample where it
+    # does not (every worker still runs at least one unit); pairs as counted by
+    # the oracle's pair counter for exactly the rows that ran
+    from dit_circular_local_amd.inputs import WORKLOADS
+
+    tiny, part = bench.cpu_oracle_runs([("tiny", 4, 5.0), ("flux1k", 8, 1e-3)])
+    assert tiny["whole_heads"] and tiny["value"] > 0
+    n_workers = tiny["worker_processes"]
+    w = WORKLOADS["tiny"]
+    assert f"{bench.admitted_pairs(w.n_text, w.grid_h, w.grid_w, 16) * n_workers} admitted pairs" in tiny["sample"]
+    assert not part["whole_heads"] and part["value"] > 0 and "proportional share" in part["sample"]
+
+
+def test_oracle_units_cover_a_head_once_in_proportion():
+    from dit_circular_local_amd.inputs import WORKLOADS
+
+    w = WORKLOADS["flux1k"]
+    for index in (0, 3):
+        u = bench._oracle_units(w, index, 8)
+        rows = [r for k, p in u if k == "text" for r in p]
+        blocks = [b for k, p in u if k == "blocks" for b in p]
+        assert sorted(rows) == list(range(w.n_text))
+        assert sorted(blocks) == [(y, x) for y in range(w.grid_h // 8) for x in range(w.grid_w // 8)]
+        # any prefix holds about the same share of text groups and block rows
+        half = u[:len(u) // 2]
+        nt = sum(k == "text" for k, _ in half) / sum(k == "text" for k, _ in u)
+        nb = sum(k == "blocks" for k, _ in half) / sum(k == "blocks" for k, _ in u)
+        assert abs(nt - nb) < 0.15

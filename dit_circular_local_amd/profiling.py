@@ -5,12 +5,12 @@ This module never touches the GPU itself.  ``collect`` starts ``rocprofv3`` as
 a child process around a command (normally ``python3 bench.py ...``), one pass
 per counter set, because the profiler does not split counters over passes;
 ``summarize`` reduces the CSV files the passes wrote to per-kernel figures and
-writes a Markdown summary plus a JSON record.  Run ``collect`` on the GPU machine
+writes a Markdown summary plus a JSON record.  Run ``collect`` on the machine with the GPU
 and ``summarize`` anywhere.
 
-    python -m dit_circular_local_amd.profiling collect --out gpurun_out/prof/fwd8k -- \\
+    python -m dit_circular_local_amd.profiling collect --out prof/fwd8k -- \\
         python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline ...
-    python -m dit_circular_local_amd.profiling summarize gpurun_out/prof/fwd8k \\
+    python -m dit_circular_local_amd.profiling summarize prof/fwd8k \\
         --kernel clear_attn_fwd_kernel --flop 1.3097e13 --bytes 6.455e9 --md profiles/x.md
 
 Passes (each its own profiler run):
@@ -299,7 +299,7 @@ def markdown(res, title: str, note: Optional[str] = None) -> str:
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
-    c = sub.add_parser("collect", help="run rocprofv3 passes around a command (on the GPU box)")
+    c = sub.add_parser("collect", help="run rocprofv3 passes around a command (on the machine with the GPU)")
     c.add_argument("--out", required=True)
     c.add_argument("--passes", default="trace,sq,sq2,fetch,write")
     c.add_argument("--copy-mib", type=int, default=1024,

@@ -351,8 +351,9 @@ def cpu_oracle_runs(jobs, seed=0):
             "sample": (f"{workers} worker processes on heads {heads}: "
                        + ("each its whole head" if whole else
                           f"each a proportional share of its head's groups of 64 text rows and rows of 8x8 image "
-                          f"blocks for ~{budget_s:g} s ({sum(x[1] for x in per)} text rows, "
-                          f"{sum(x[2] for x in per)} block rows of {nby} per head, over all workers)")
+                          f"blocks for ~{budget_s:g} s ({sum(x[1] for x in per)} text rows and "
+                          f"{sum(x[2] for x in per)} block rows over all workers; a head has {w.n_text} text rows "
+                          f"and {nby} block rows)")
                        + f", r={radius}; {pairs} admitted pairs in {secs:.2f} s; fp64 numpy"),
             "seconds": secs,
             "whole_heads": whole,

@@ -161,6 +161,45 @@ def test_flux_8192_sampled_rows():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("r", [8, 32])
+def test_flux_8192_fp32_sampled_gradients(r):
+    """512x512 grid + 512 text, 24 heads, fp32 inputs with the FLUX recipe, in
+    the benchmark's launch shape: dq of query blocks and dk, dv of image keys
+    on the tilings' boundaries (16 x 8 query tiles, 4 x 8 sub- and key tiles,
+    the grid's edges and corners) and in the middle, for the first and last
+    heads, against the oracle at the fp32 bar.  A key tile dropped from, or
+    added to, a gradient walk moves these entries far beyond 1e-5."""
+    w = WORKLOADS["flux8k"]
+    q, k, v = make_qkv(w.B, w.H, w.n_text, w.grid_h, w.grid_w, w.d, "fp32", seed=90 + r, rms_norm=True,
+                       scale=1.0, device="cuda")
+    do = make_dout(w.B, w.H, w.n, w.d, "fp32", 90 + r, scale=1.0, device="cuda")
+    r2 = r * r
+    dq, dk, dv = _gpu_grads(q, k, v, do, w.n_text, w.grid_h, w.grid_w, r2)
+    g = w.grid_h
+    # 8 x 8 oracle blocks: corners, edges, blocks straddling 16-row tile and
+    # 8-column tile boundaries, the middle
+    blocks = [(0, 0), (0, 63), (63, 0), (63, 63), (1, 1), (2, 2), (3, 31), (32, 32), (31, 40)]
+    text_rows = [0, 1, 255, w.n_text - 1]
+    key_cells = [(0, 0), (0, 7), (3, 8), (4, 9), (15, 15), (16, 16), (255, 256), (g - 1, g - 1), (g - 4, 3)]
+    keys = [w.n_text + y * g + x for y, x in key_cells]
+    for h in (0, 23):
+        qh, kh, vh, dh = (_np(t[0, h]) for t in (q, k, v, do))
+        ref_dq, _, _ = attention_backward_head(qh, kh, vh, dh, w.n_text, g, g, r2, text_rows=text_rows,
+                                               blocks=blocks)
+        rows = text_rows + [w.n_text + (8 * by + y) * g + 8 * bx + x for by, bx in blocks
+                            for y in range(8) for x in range(8)]
+        err = np.abs(_np(dq[0, h, rows]) - ref_dq[rows])
+        i = int(err.max(axis=1).argmax())
+        assert err.max() <= FP32_TOL, f"r={r} dq head {h}: max-abs {err.max():.3e} at row {rows[i]}"
+        ref_dk, ref_dv = key_grads(qh, kh, vh, dh, w.n_text, g, g, r2, keys)
+        for name, gt, rf in (("dk", dk, ref_dk), ("dv", dv, ref_dv)):
+            err = np.abs(_np(gt[0, h, keys]) - rf)
+            i = int(err.max(axis=1).argmax())
+            assert err.max() <= FP32_TOL, f"r={r} {name} head {h}: max-abs {err.max():.3e} at key {key_cells[i]}"
+    del q, k, v, do, dq, dk, dv
+    torch.cuda.empty_cache()
+
+
 def test_bwd_rejects_bad_arguments():
     q, k, v, do = _inputs("bf16", 1, 1, 8, 4, 4, 64, 6)
     out, lse = ca.fwd(q, k, v, 8, 4, 4, radius=1, return_lse=True)

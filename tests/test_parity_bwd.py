@@ -13,7 +13,7 @@ does; the oracle differentiates its own forward.  Bars:
   output O it reads for D = dO . O carries the forward's own bf16 error.  The
   summed rounding errors stay below a few units of 2^-9 of the largest entry
   (at most 3.3 x 2^-9 measured over the cases here); 2^-6 = 8 x 2^-9 leaves a
-  margin of 2.5x and stays far below what a wrong index or sign produces
+  margin of 2.4x and stays far below what a wrong index or sign produces
   (order 1).
 * tile walks and split counts never change results beyond these bars, and two
   runs are bit-identical (no atomics).

@@ -268,3 +268,24 @@ def test_noalloc_forward_checks_before_any_hip_call():
     assert rc == ca.CLEAR_ENOMEM and "no-alloc scratch" in ca.last_error()
     rc = _noalloc(splits=64, B=1, H=24, n_text=512, gh=64, gw=64, r2=256)
     assert rc == ca.CLEAR_ENOMEM and "text splits" in ca.last_error()
+
+
+def test_plain_c_caller(tmp_path):
+    """The header compiles as C99 with warnings as errors, and a C program
+    linked against the library gets the documented results from calls that
+    need no GPU."""
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    here = os.path.dirname(os.path.abspath(__file__))
+    libdir = os.path.dirname(ca.LIB_PATH)
+    exe = str(tmp_path / "abi_check")
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                    "-I", os.path.dirname(HEADER), os.path.join(here, "c_abi", "abi_check.c"),
+                    "-L", libdir, "-lclear_attn", f"-Wl,-rpath,{libdir}", "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "tile map entries 2" in r.stdout and r.stdout.rstrip().endswith("ok")

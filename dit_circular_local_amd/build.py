@@ -62,7 +62,8 @@ def kernel_source_hash() -> str:
 def build_command(out: str = LIB):
     return [
         HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-        "-Wall", "-Wno-unused-function",
+        # warnings are errors (unused parameters aside: engines share signatures)
+        "-Wall", "-Wextra", "-Wno-unused-parameter", "-Wno-unused-function", "-Werror",
         *DEVICE_FLAGS,
         "-I", INCLUDE, "-I", CSRC,
         *[os.path.join(CSRC, s) for s in SOURCES],

@@ -90,3 +90,24 @@ def test_oracle_units_cover_a_head_once_in_proportion():
         nt = sum(k == "text" for k, _ in half) / sum(k == "text" for k, _ in u)
         nb = sum(k == "blocks" for k, _ in half) / sum(k == "blocks" for k, _ in u)
         assert abs(nt - nb) < 0.15
+
+
+def test_committed_profiles_match_the_kernel_sources():
+    # the forward figures bench.py reports beside its own timing come from
+    # profiles taken on the current kernel sources and device flags; a kernel
+    # change without new profiles fails here instead of dropping them silently
+    for r in (32, 8):
+        e = bench.load_profile("flux8k", r)
+        assert e is not None, f"profiles/traffic.json has no entry for the current sources at r={r}"
+        assert e["hbm_bytes_per_launch"] > 0 and 0 < e["mfma_busy"] < 1 and e["kernel_ms"] > 0
+
+
+def test_profile_of_other_sources_is_not_used(tmp_path, monkeypatch):
+    import json
+
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "traffic.json").write_text(json.dumps(
+        {"flux8k_r32": {"kernel_source_hash": "0" * 16, "hbm_bytes_per_launch": 1.0}}))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.load_profile("flux8k", 32) is None
+    assert bench.load_profile("flux8k", 8) is None

@@ -253,13 +253,16 @@ def _repo_relative(cmd: str) -> str:
     return re.sub(r"/\S*?/repo(?=/)", "$REPO", cmd)
 
 
-def markdown(res, title: str, note: Optional[str] = None) -> str:
+def markdown(res, title: str, note: Optional[str] = None, summary_cmd: Optional[str] = None) -> str:
     """A short Markdown summary of ``summarize``'s record, or of several
-    records of one run (one section per kernel)."""
+    records of one run (one section per kernel); ``summary_cmd`` is the
+    command that wrote it."""
     recs = [res] if isinstance(res, dict) else list(res)
     lines = [f"# {title}", ""]
     if note:
         lines += [note, ""]
+    if summary_cmd:
+        lines += [f"Summary written by `{_repo_relative(summary_cmd)}` from the CSV files of the passes below.", ""]
     lines += ["Commands (each pass its own profiler run, from /tmp; `$REPO` is the repository root):", ""]
     for p in ("trace", "sq", "sq2", "fetch", "write", "copy_fetch", "copy_write"):
         cmdf = os.path.join(recs[0]["root"], f"{p}.cmd")
@@ -344,7 +347,16 @@ def main(argv=None) -> int:
     if a.record and len(recs) != 1:
         ap.error("--record takes one kernel")
     res = recs[0] if len(recs) == 1 else recs
-    md = markdown(res, a.title, a.note)
+    # the command line, with the title and note texts elided
+    shown, skip = [], False
+    for x in (argv if argv is not None else sys.argv[1:]):
+        if skip:
+            shown.append("...")
+            skip = False
+            continue
+        shown.append(x)
+        skip = x in ("--title", "--note")
+    md = markdown(res, a.title, a.note, "python -m dit_circular_local_amd.profiling " + shlex.join(shown))
     if a.md:
         with open(a.md, "w") as f:
             f.write(md + "\n")

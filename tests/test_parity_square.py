@@ -12,6 +12,7 @@ import torch
 import dit_circular_local_amd as ca
 from dit_circular_local_amd.inputs import WORKLOADS, make_qkv, workload_qkv
 from oracle import attention, attention_rows, tile_map_bruteforce
+from window_box import box_reference
 
 pytestmark = pytest.mark.gpu
 
@@ -94,5 +95,31 @@ def test_square_flux_8192_sampled_rows():
                                 rows, window="square")
         err = np.abs(_np(out[0, h, rows]) - ref).max()
         assert err <= 2e-2, f"head {h}: max-abs {err:.3e}"
+    del q, k, v, out
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("r", [8, 32])
+def test_square_flux_8192_fp32_boundary_rows(r):
+    """512x512 grid + 512 text, 24 heads in one launch, fp32 inputs with the
+    FLUX recipe, square window: rows of heads 0 and 23 on the tilings'
+    boundaries, the grid's edges and corners, and random rows, against the
+    window-box reference at 1e-5, where one key too many or too few shows."""
+    w = WORKLOADS["flux8k"]
+    q, k, v = make_qkv(w.B, w.H, w.n_text, w.grid_h, w.grid_w, w.d, "fp32", seed=120 + r, rms_norm=True,
+                       scale=1.0, device="cuda")
+    out = ca.fwd(q, k, v, w.n_text, w.grid_h, w.grid_w, radius=r, window="square")
+    torch.cuda.synchronize()
+    g = w.grid_h
+    rng = np.random.default_rng(r)
+    ys = sorted({0, 1, 3, 4, 15, 16, 31, 32, g // 2, g - 17, g - 16, g - 5, g - 4, g - 1})
+    xs = sorted({0, 1, 7, 8, 15, 16, g // 2, g - 9, g - 8, g - 1})
+    cells = sorted(set([(y, x) for y in ys for x in xs] + [tuple(int(c) for c in rc)
+                                                         for rc in rng.integers(0, g, (30, 2))]))
+    for h in (0, 23):
+        rows, ref = box_reference(q[0, h], k[0, h], v[0, h], w.n_text, g, g, r * r, cells, window="square")
+        err = np.abs(_np(out[0, h, rows]) - ref)
+        i = int(err.max(axis=1).argmax())
+        assert err.max() <= 1e-5, f"r={r} head {h}: max-abs {err.max():.3e} at cell {cells[i]}"
     del q, k, v, out
     torch.cuda.empty_cache()

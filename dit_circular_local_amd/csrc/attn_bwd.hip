@@ -14,7 +14,7 @@
 //    dQ_i  = sum_j dS_ij k_j / sqrt(d),   dK_j = sum_i dS_ij q_i / sqrt(d)
 //
 // Launches (one stream):
-//  1. prep: per row, (lse2, D) from the forward's LSE, O and dO;
+//  1. prep: per row, (lse2, -D) from the forward's LSE, O and dO;
 //  2. dK/dV, key-centred.  Image workgroups own a 16 x 8 cell key tile, each
 //     wavefront a 4 x 8 key sub-tile (32 keys) with its K rows in registers
 //     and its V rows in registers (fp32) or in an LDS region of its own (bf16,
@@ -37,7 +37,7 @@
 //           dV^T += dO^T . P,  dK^T += Q^T . dS   A = dO^T, Q^T (LDS transpose reads)
 //   dQ:     S^T = K . Q^T, dP^T = V . dO^T    A = K, V rows (LDS), B = Q, dO (VGPRs)
 //           dQ^T += K^T . dS^T                A = K^T (LDS transpose reads)
-// so every row statistic (lse2, D) of the key-centred kernel is per register
+// so every row statistic (lse2, -D) of the key-centred kernel is per register
 // and of the query-centred kernel per lane.
 #include "attn_common.h"
 
@@ -323,7 +323,7 @@ struct BwdF32 {
 // E::kBlockPitch apart), and block b of a region is filled by wavefront b % 4.
 // Each lane keeps the byte offset of its slot's piece from the chunk's first
 // token, for a dense token range and for a 4 x 8 cell tile (rows gw apart).
-// The key-centred kernel also stages the chunk's (lse2, D) pairs: one 4-byte
+// The key-centred kernel also stages the chunk's (lse2, -D) pairs: one 4-byte
 // load per lane, lane l fetching component l / 32 of row l % 32; every
 // wavefront keeps its own copy.
 
